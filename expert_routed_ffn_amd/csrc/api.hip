@@ -1,0 +1,187 @@
+// api.hip -- the C ABI entry points: argument checks, workspace sizes, and
+// hand-off to the kernel launchers.  A failing check enqueues nothing.
+#include <cstdio>
+#include <string>
+
+#include "internal.hpp"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+moe_status fail(moe_status st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+moe_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+moe_status check_launch(const char* what) { return check_hip(hipGetLastError(), what); }
+
+static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+
+BlobLayout blob_layout(int H, int I, int bits) {
+  const int64_t gu_codes = (int64_t)I * H * bits / 8, gu_sm = (int64_t)I * (H / 32) * 4;
+  const int64_t d_codes = (int64_t)H * I * bits / 8, d_sm = (int64_t)H * (I / 32) * 4;
+  BlobLayout L;
+  int64_t o = 0;
+  L.gate_codes = o; o = up256(o + gu_codes);
+  L.gate_sm = o;    o = up256(o + gu_sm);
+  L.up_codes = o;   o = up256(o + gu_codes);
+  L.up_sm = o;      o = up256(o + gu_sm);
+  L.down_codes = o; o = up256(o + d_codes);
+  L.down_sm = o;    o = up256(o + d_sm);
+  L.bytes = o;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  snprintf(buf, sizeof buf, f, a, b, c);
+  return buf;
+}
+
+moe_status check_ek(const char* fn, int E, int k) {
+  if (E < 1 || E > kMaxE) return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": E=%lld outside [1, 1024]", E));
+  if (k < 1 || k > kMaxK || k > E)
+    return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": k=%lld outside [1, min(16, E=%lld)]", k, E));
+  return MOE_OK;
+}
+
+moe_status check_shape(const char* fn, int H, int I, int bits) {
+  if (bits != 2 && bits != 4) return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": bits=%lld (2 or 4)", bits));
+  if (H < 32 || H > 16384 || H % 32)
+    return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": H=%lld (multiple of 32 in [32, 16384])", H));
+  if (I < 32 || I > 8192 || I % 32)
+    return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": I=%lld (multiple of 32 in [32, 8192])", I));
+  return MOE_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE";
+    case MOE_EHIP: return "MOE_EHIP";
+    case MOE_ENOTPINNED: return "MOE_ENOTPINNED";
+    case MOE_ECAPACITY: return "MOE_ECAPACITY";
+  }
+  return "unknown moe_status";
+}
+
+size_t moe_expert_bytes(int H, int I, int bits) {
+  if (check_shape("moe_expert_bytes", H, I, bits) != MOE_OK) return 0;
+  return (size_t)blob_layout(H, I, bits).bytes;
+}
+
+moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_route_topk: T < 0");
+  if (moe_status st = check_ek("moe_route_topk", E, k)) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !w) return fail(MOE_EINVAL, "moe_route_topk: null pointer");
+  return launch_route_topk(logits, T, E, k, ids, w, stream);
+}
+
+size_t moe_dispatch_workspace_bytes(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return dispatch_ws_bytes(T * k, E);
+}
+
+moe_status moe_dispatch(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
+                        int32_t* assign_pos, int32_t* active, int32_t* n_active, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_dispatch: T < 0");
+  if (moe_status st = check_ek("moe_dispatch", E, k)) return st;
+  if ((int64_t)T * k > (int64_t)1 << 24) return fail(MOE_EUNSUPPORTED, "moe_dispatch: T*k above 2^24");
+  if (!offsets || !n_active) return fail(MOE_EINVAL, "moe_dispatch: null pointer");
+  if (T > 0 && (!ids || !sorted_assign || !assign_pos || !active))
+    return fail(MOE_EINVAL, "moe_dispatch: null pointer");
+  const size_t need = dispatch_ws_bytes(T * k, E);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_EWORKSPACE, fmt("moe_dispatch: workspace %lld bytes, needs %lld", (long long)ws_bytes,
+                                    (long long)need));
+  return launch_dispatch(ids, T * k, E, offsets, sorted_assign, assign_pos, active, n_active, ws, stream);
+}
+
+static moe_ffn_path resolve_path(moe_ffn_path p, int T) {
+  if (p == MOE_PATH_AUTO) return T <= 8 ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+  return p;
+}
+
+size_t moe_expert_ffn_workspace_bytes(const moe_qlayer* q, int T, int k, moe_ffn_path path) {
+  if (!q || T < 0 || k < 1) return 0;
+  const int n = T * k;
+  if (resolve_path(path, T) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(n, q->I);
+  return ffn_mfma_ws_bytes(n, q->E, q->I);
+}
+
+moe_status moe_expert_ffn_q(const moe_qlayer* q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
+                            const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
+                            moe_dtype y_t, moe_ffn_path path, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "moe_expert_ffn_q";
+  if (!q) return fail(MOE_EINVAL, "moe_expert_ffn_q: null moe_qlayer");
+  if (T < 0) return fail(MOE_EINVAL, "moe_expert_ffn_q: T < 0");
+  if (moe_status st = check_ek(fn, q->E, k)) return st;
+  if (moe_status st = check_shape(fn, q->H, q->I, q->bits)) return st;
+  if (x_t != MOE_F32 && x_t != MOE_BF16) return fail(MOE_EINVAL, "moe_expert_ffn_q: x dtype");
+  if (y_t != MOE_F32 && y_t != MOE_BF16) return fail(MOE_EINVAL, "moe_expert_ffn_q: y dtype");
+  if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_MFMA)
+    return fail(MOE_EINVAL, "moe_expert_ffn_q: path");
+  if ((int64_t)T * k > (int64_t)1 << 24) return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_q: T*k above 2^24");
+  if (T == 0) return MOE_OK;
+  if (!q->base || !x || !offsets || !sorted_assign || !active || !n_active || !y)
+    return fail(MOE_EINVAL, "moe_expert_ffn_q: null pointer");
+  const int64_t eb = blob_layout(q->H, q->I, q->bits).bytes;
+  if (q->stride < eb || q->stride % 256)
+    return fail(MOE_EINVAL, fmt("moe_expert_ffn_q: stride %lld (needs >= %lld and a multiple of 256)", q->stride, eb));
+  if (!aligned(q->base, 256)) return fail(MOE_EINVAL, "moe_expert_ffn_q: base not 256-byte aligned");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_EINVAL, "moe_expert_ffn_q: x or y not 16-byte aligned");
+  const moe_ffn_path p = resolve_path(path, T);
+  const size_t need = moe_expert_ffn_workspace_bytes(q, T, k, p);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_EWORKSPACE, fmt("moe_expert_ffn_q: workspace %lld bytes, needs %lld", (long long)ws_bytes,
+                                    (long long)need));
+  if (p == MOE_PATH_GEMV)
+    return launch_ffn_gemv(*q, x, x_t, T, k, offsets, sorted_assign, active, n_active, y, y_t, ws, stream);
+  return launch_ffn_mfma(*q, x, x_t, T, k, offsets, sorted_assign, active, n_active, y, y_t, ws, stream);
+}
+
+moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,
+                       moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t stream) {
+  if (T < 0 || H < 1) return fail(MOE_EINVAL, "moe_combine: T < 0 or H < 1");
+  if (k < 1 || k > kMaxK) return fail(MOE_EUNSUPPORTED, "moe_combine: k outside [1, 16]");
+  if (H % 4) return fail(MOE_EUNSUPPORTED, "moe_combine: H must be a multiple of 4");
+  if (y_t != MOE_F32 && y_t != MOE_BF16) return fail(MOE_EINVAL, "moe_combine: y dtype");
+  if (residual && r_t != MOE_F32 && r_t != MOE_BF16) return fail(MOE_EINVAL, "moe_combine: residual dtype");
+  if (T == 0) return MOE_OK;
+  if (!y || !w || !out) return fail(MOE_EINVAL, "moe_combine: null pointer");
+  const uintptr_t r_align = r_t == MOE_F32 ? 16 : 8;
+  if (!aligned(y, 16) || !aligned(out, 16) || (residual && !aligned(residual, r_align)) ||
+      (out_bf16 && !aligned(out_bf16, 8)))
+    return fail(MOE_EINVAL, "moe_combine: misaligned buffer");
+  return launch_combine(y, y_t, w, T, k, H, residual, r_t, out, out_bf16, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// combine.hip -- weighted sum of each token's k expert rows back in token order.
+//
+// out[t][c] = residual[t][c] + sum_{j=0}^{k-1} w[t][j] * y[t*k + j][c], j ascending,
+// in fp32; optionally also the bf16 (round to nearest even) of out, which is
+// the next layer's input when layers are chained.  Each thread owns four
+// consecutive columns (one 16-byte load per fp32 row), so the pass is a plain
+// coalesced stream over y.
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+struct F4 {
+  float v[4];
+};
+
+__device__ __forceinline__ F4 load4(const float* p) {
+  const float4 q = *reinterpret_cast<const float4*>(p);
+  return {{q.x, q.y, q.z, q.w}};
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ F4 load4(const uint16_t* p) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  return {{bf16_bits_to_f32(q.x & 0xFFFFu), bf16_bits_to_f32(q.x >> 16), bf16_bits_to_f32(q.y & 0xFFFFu),
+           bf16_bits_to_f32(q.y >> 16)}};
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename YT, typename RT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, const float* __restrict__ w, int T,
+                                                      int k, int H, const RT* __restrict__ residual,
+                                                      float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  F4 acc = {{0.f, 0.f, 0.f, 0.f}};
+  if (residual) acc = load4(residual + (size_t)t * H + c);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const F4 v = load4(y + ((size_t)t * k + j) * H + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc.v[i] += wj * v.v[i];
+  }
+  *reinterpret_cast<float4*>(out + (size_t)t * H + c) = make_float4(acc.v[0], acc.v[1], acc.v[2], acc.v[3]);
+  if (out_bf16) {
+    uint2 b;
+    b.x = f32_to_bf16_rne(acc.v[0]) | (f32_to_bf16_rne(acc.v[1]) << 16);
+    b.y = f32_to_bf16_rne(acc.v[2]) | (f32_to_bf16_rne(acc.v[3]) << 16);
+    *reinterpret_cast<uint2*>(out_bf16 + (size_t)t * H + c) = b;
+  }
+}
+
+template <typename YT>
+void launch_r(const YT* y, const float* w, int T, int k, int H, const void* residual, moe_dtype r_t, float* out,
+              uint16_t* out_bf16, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(H / 4, 256), (unsigned)T), block(256);
+  if (residual && r_t == MOE_BF16)
+    combine_kernel<YT, uint16_t><<<grid, block, 0, s>>>(y, w, T, k, H, (const uint16_t*)residual, out, out_bf16);
+  else
+    combine_kernel<YT, float><<<grid, block, 0, s>>>(y, w, T, k, H, (const float*)residual, out, out_bf16);
+}
+
+}  // namespace
+
+moe_status launch_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,
+                          moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t s) {
+  if (T > 65535) return fail(MOE_EUNSUPPORTED, "moe_combine: T above 65535");
+  if (y_t == MOE_BF16)
+    launch_r((const uint16_t*)y, w, T, k, H, residual, r_t, out, out_bf16, s);
+  else
+    launch_r((const float*)y, w, T, k, H, residual, r_t, out, out_bf16, s);
+  return check_launch("combine");
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+moe_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return MOE_OK;
+  const int blocks = (int)std::min<int64_t>(1024, ceil_div(n, 256));
+  fill_i32_kernel<<<blocks, 256, 0, s>>>(p, n, v);
+  return check_launch("fill_i32");
+}
+
+}  // namespace moe

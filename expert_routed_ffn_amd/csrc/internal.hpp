@@ -1,0 +1,56 @@
+// internal.hpp -- declarations shared by the library's own translation units.
+// Nothing here is part of the C ABI (that is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "moe.h"
+
+namespace moe {
+
+// Thread-local error text behind moe_last_error().
+void set_error(const std::string& msg);
+moe_status fail(moe_status st, const std::string& msg);
+moe_status check_hip(hipError_t e, const char* what);
+// Reports a launch error (hipGetLastError) as MOE_EHIP.
+moe_status check_launch(const char* what);
+
+// Byte offsets of the six planes of an expert blob and its size.
+struct BlobLayout {
+  int64_t gate_codes, gate_sm, up_codes, up_sm, down_codes, down_sm, bytes;
+};
+BlobLayout blob_layout(int H, int I, int bits);
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+
+// ---- launchers (each returns hipGetLastError()-based status) ---------------
+
+moe_status launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+
+size_t dispatch_ws_bytes(int n, int E);
+moe_status launch_dispatch(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* sorted_assign,
+                           int32_t* assign_pos, int32_t* active, int32_t* n_active, void* ws, hipStream_t s);
+
+size_t ffn_gemv_ws_bytes(int n_assign, int I);
+moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
+                           const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
+                           moe_dtype y_t, void* ws, hipStream_t s);
+
+size_t ffn_mfma_ws_bytes(int n_assign, int E, int I);
+moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
+                           const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
+                           moe_dtype y_t, void* ws, hipStream_t s);
+
+moe_status launch_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,
+                          moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t s);
+
+moe_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moe

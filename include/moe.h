@@ -1,0 +1,240 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts FFN layer.
+ *
+ * The layer: a router picks, per token, the k experts with the largest logits
+ * and weights them by the softmax of those k logits; the tokens are grouped by
+ * expert; each expert runs a SwiGLU FFN whose weights are stored in a low-bit
+ * block format; the expert outputs are summed back in token order with the
+ * gate weights.  Sources for what is computed:
+ *   - only a few experts per token run (10 of 512 in each of 48 layers of the
+ *     125B model), chosen by the router: Strata feature (tech.hub77a.com),
+ *     summary table row "핵심 기법" and section "2. 왜 대단한가" (1);
+ *   - the compute path branches on the routing result: resident experts are
+ *     used at once, the rest are first moved in from host memory: ibid. (2);
+ *     Janas-LLM item (onedev.kr/items/2196): repeat experts stay cached;
+ *   - a draft-and-verify step checks 1 + d guessed tokens in one pass, and the
+ *     prompt path reads up to 8,192 tokens per chunk: Strata feature (3);
+ *   - 2-bit class weights (Q2_0) are the fast size: Strata feature, section
+ *     "3. 바로 써먹기", speed table.
+ *
+ * Weight format (b = 2 or 4).  A matrix [R x K] (K % 32 == 0) is split into
+ * blocks of 32 weights along K.  Each block carries an IEEE binary16 scale s
+ * and min m; weight = s * q + m for the block's b-bit unsigned codes q.
+ *   code plane: row r is K*b/32 little-endian uint32 words; word w holds
+ *     columns w*(32/b) ... (w+1)*(32/b) - 1; column c of a word sits at bit
+ *     16*(c % 2) + b*(c / 2), so even columns fill the low halfword and odd
+ *     columns the high halfword;
+ *   s/m plane: row r is K/32 uint32 words, scale in bits 0-15, min in 16-31;
+ *   expert blob: Wg codes, Wg s/m, Wu codes, Wu s/m, Wd codes, Wd s/m, each
+ *     plane starting on a 256-byte boundary; Wg and Wu are [I x H], Wd is
+ *     [H x I]; the blob is moe_expert_bytes(H, I, b) bytes.
+ *
+ * Conventions for every call:
+ *   - Pointers are device memory owned by the caller unless marked "host".
+ *     The library never allocates device memory; scratch space is passed in
+ *     and sized by the *_workspace_bytes queries.
+ *   - Work is enqueued on the given stream and runs asynchronously; inputs
+ *     must stay valid until the stream reaches it.  Nothing blocks the host
+ *     except moe_slot_table_resolve/preload, which say so.
+ *   - Arguments are checked on the host before anything is enqueued; a call
+ *     that returns an error has enqueued nothing.  moe_last_error() returns a
+ *     thread-local message for the last failing call on this thread.
+ *   - A HIP runtime or launch failure is reported as MOE_EHIP.
+ *   - Limits: 1 <= E <= 1024, 1 <= k <= min(16, E), H % 32 == 0 and
+ *     I % 32 == 0 with 32 <= H <= 16384 and 32 <= I <= 8192, b in {2, 4},
+ *     T >= 0 (T == 0 enqueues nothing and returns MOE_OK).
+ *   - Device buffers that the kernels read with 128-bit loads (expert blobs,
+ *     activations) must be 16-byte aligned; the expert stride must be a
+ *     multiple of 256.
+ *   - Logits must be finite; NaN or infinite logits give unspecified (but
+ *     memory-safe) routing.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* a null pointer, a negative size, inconsistent sizes */
+  MOE_EUNSUPPORTED = 2, /* sizes outside the limits above */
+  MOE_EWORKSPACE = 3,   /* the workspace is smaller than the query returned */
+  MOE_EHIP = 4,         /* a HIP runtime or kernel launch error */
+  MOE_ENOTPINNED = 5,   /* a host buffer that must be page-locked is not */
+  MOE_ECAPACITY = 6     /* the slot table cannot hold the active set */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which expert-FFN kernels to run.  AUTO picks GEMV for T <= 8 and MFMA above. */
+typedef enum moe_ffn_path {
+  MOE_PATH_AUTO = 0,
+  MOE_PATH_GEMV = 1, /* fused dequant-GEMV, fp32 throughout: decode and verify steps */
+  MOE_PATH_MFMA = 2  /* weights dequantized to bf16 in LDS, bf16 MFMA, fp32 accumulate: prefill */
+} moe_ffn_path;
+
+/* One layer's experts.  Expert e's blob is at base + idx(e) * stride where
+ * idx(e) = slot_map[e] when slot_map is not NULL, else e.  slot_map (device,
+ * [E]) is what a slot table maintains for one layer; an entry below zero
+ * means "not resident" and makes that expert's output rows NaN. */
+typedef struct moe_qlayer {
+  int E, H, I, bits;
+  const void* base;         /* device, 256-byte aligned */
+  int64_t stride;           /* bytes, >= moe_expert_bytes(H, I, bits), multiple of 256 */
+  const int32_t* slot_map;  /* device, NULL or [E] */
+} moe_qlayer;
+
+int moe_abi_version(void);
+const char* moe_last_error(void);
+const char* moe_status_string(moe_status st);
+
+/* Bytes of one expert blob: 3*H*I*(b/8 + 4/32) plus plane padding to 256 B. */
+size_t moe_expert_bytes(int H, int I, int bits);
+
+/*
+ * moe_route_topk -- top-k expert selection and gate weights.
+ * Passage: Strata feature, summary row "핵심 기법" and section "2. 왜 대단한가"
+ * (1)-(2) (the router picks a few experts per token and only those run).
+ *   logits  [T x E] fp32, row-major.
+ *   ids     [T x k] int32 out: the k largest logits of each row in descending
+ *           order; equal logits rank the lower expert id first; -0.0 equals +0.0.
+ *   w       [T x k] fp32 out: w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ *           over the k selected logits (sums to 1 up to rounding).
+ * Errors: MOE_EINVAL (null pointers with T > 0), MOE_EUNSUPPORTED (E, k out of range).
+ */
+moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream);
+
+/*
+ * moe_dispatch -- group the n = T*k assignments a = t*k + j by expert.
+ * Passage: the tokens routed to one expert are computed together (Strata
+ * feature, section "2. 왜 대단한가" (2): the compute path follows the routing).
+ * The order is unique: ascending expert, and ascending a inside an expert.
+ *   ids           [T x k] int32 in; ids outside [0, E) are dropped (not
+ *                 counted, their assign_pos entry is -1).
+ *   offsets       [E + 1] out: offsets[e] = number of kept assignments with expert < e.
+ *   sorted_assign [n] out: the assignment at each sorted position (entries past
+ *                 offsets[E] are left unchanged).
+ *   assign_pos    [n] out: inverse of sorted_assign (-1 for dropped ones).
+ *   active        [min(E, n)] out: experts with at least one assignment, ascending.
+ *   n_active      [1] out: how many entries of active are set.
+ *   ws            device scratch of at least moe_dispatch_workspace_bytes(T, k, E) bytes.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE.
+ */
+size_t moe_dispatch_workspace_bytes(int T, int k, int E);
+moe_status moe_dispatch(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* sorted_assign,
+                        int32_t* assign_pos, int32_t* active, int32_t* n_active, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * moe_expert_ffn_q -- SwiGLU FFN of every routed (token, expert) pair.
+ * Passage: only the selected experts' weights are read (Strata feature,
+ * section "2. 왜 대단한가" (1)); 2-bit class weights (speed table, section
+ * "3. 바로 써먹기"); verify steps of 1 + d tokens and 8,192-token prompt
+ * chunks (section "2. 왜 대단한가" (3)).
+ * For each sorted position p in [offsets[e], offsets[e+1]) of each active
+ * expert e, with a = sorted_assign[p] and t = a / k:
+ *   g = Wg x[t], u = Wu x[t], h = silu(g) * u, y[a] = Wd h.
+ *   x        [T x H], dtype x_t (MOE_F32 or MOE_BF16), 16-byte aligned.
+ *   y        [T x k x H] out, dtype y_t; rows of dropped assignments are untouched.
+ *   path     MOE_PATH_GEMV keeps g, u, h and the sums in fp32 (the bf16 dot
+ *            instructions see x exactly, and fp32 values as a sum of two bf16
+ *            parts); MOE_PATH_MFMA rounds the decoded weights and h to bf16
+ *            and accumulates in fp32.
+ *   ws       device scratch of at least moe_expert_ffn_workspace_bytes(...) bytes.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE.
+ */
+size_t moe_expert_ffn_workspace_bytes(const moe_qlayer* q, int T, int k, moe_ffn_path path);
+moe_status moe_expert_ffn_q(const moe_qlayer* q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
+                            const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
+                            moe_dtype y_t, moe_ffn_path path, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- weighted sum of the k expert rows of each token.
+ * out[t][c] = residual[t][c] + sum_{j=0}^{k-1} w[t][j] * y[t][j][c], j ascending, fp32.
+ *   y         [T x k x H], dtype y_t.
+ *   w         [T x k] fp32 gate weights.
+ *   residual  NULL or [T x H], dtype r_t.
+ *   out       [T x H] fp32 out.
+ *   out_bf16  NULL or [T x H] out: bf16 (round to nearest even) of out, as raw bits.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED.
+ */
+moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,
+                       moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t stream);
+
+/*
+ * Resident-expert slot table.
+ * Passage: the most-called experts stay resident in GPU memory while all of
+ * them sit in host RAM; a routed expert that is resident is used at once and
+ * any other is first moved in (Strata feature, section "2. 왜 대단한가" (2));
+ * repeat experts are kept cached (Janas-LLM item); part of host memory is
+ * locked for the graphics card (Strata feature, section "3. 바로 써먹기").
+ *
+ * The table manages n_slots device slots of expert_bytes each for the L*E
+ * (layer, expert) blobs whose master copies sit in page-locked host memory:
+ * blob (l, e) at host_experts + (l*E + e) * expert_bytes.  slot_map[l*E + e]
+ * (device) holds the slot of (l, e) or -1.  Pass slots as moe_qlayer.base,
+ * expert_bytes as .stride and slot_map + l*E as .slot_map.
+ * Policy: least recently used over (layer, expert); misses of one resolve
+ * are served in ascending expert order; a slot used by the same resolve is
+ * never a victim.  The policy changes only timing, never results.
+ * Copies and map updates are enqueued on the given stream, so kernels that
+ * follow on that stream see them.  A table serves one stream and one host
+ * thread at a time.
+ */
+typedef struct moe_slot_table moe_slot_table;
+
+typedef struct moe_slot_stats {
+  uint64_t hits, misses, bytes_h2d, resolves, evictions;
+} moe_slot_stats;
+
+/* MOE_ENOTPINNED when host_experts is not page-locked host memory;
+ * expert_bytes must be a multiple of 256; slots and slot_map are device memory
+ * of n_slots * expert_bytes bytes and L*E int32.  The map is set to -1 on
+ * `stream` (enqueued; ordered before later work on it). */
+moe_status moe_slot_table_create(int L, int E, int n_slots, size_t expert_bytes, const void* host_experts, void* slots,
+                                 int32_t* slot_map, hipStream_t stream, moe_slot_table** out);
+
+/* Make the given (layer, expert) pairs resident (host array of 2*n int32:
+ * layer, expert, ...), in order, evicting least recently used slots.  Copies
+ * are enqueued on stream; the call returns after enqueueing. */
+moe_status moe_slot_table_preload(moe_slot_table* t, const int32_t* layer_expert, int n, hipStream_t stream);
+
+/* Make every expert in active[0 .. *n_active) of `layer` resident.  active and
+ * n_active are device arrays written earlier on `stream` (moe_dispatch); this
+ * call copies them to the host and waits for them (it blocks the host until
+ * the stream has reached this point), then enqueues the miss copies and the
+ * map update on stream.  MOE_ECAPACITY if n_active > n_slots. */
+moe_status moe_slot_table_resolve(moe_slot_table* t, int layer, const int32_t* active, const int32_t* n_active,
+                                  hipStream_t stream);
+
+moe_status moe_slot_table_stats(const moe_slot_table* t, moe_slot_stats* out);
+
+/* Host view of the map: out (host, [L*E]) = slot of each (layer, expert) or -1. */
+moe_status moe_slot_table_map_host(const moe_slot_table* t, int32_t* out);
+
+void moe_slot_table_destroy(moe_slot_table* t);
+
+/*
+ * Host-only slot table for exercising the policy without a GPU.  Every copy
+ * the real table would enqueue is reported to copy_fn(user, slot, layer,
+ * expert) instead; resolve takes a host array of active experts.
+ */
+typedef void (*moe_copy_fn)(void* user, int slot, int layer, int expert);
+moe_status moe_slot_table_create_host(int L, int E, int n_slots, moe_copy_fn copy_fn, void* user,
+                                      moe_slot_table** out);
+moe_status moe_slot_table_resolve_host(moe_slot_table* t, int layer, const int32_t* active, int n_active);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

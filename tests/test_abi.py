@@ -1,0 +1,97 @@
+"""The C ABI library loads without a GPU, exports what include/moe.h declares, and
+rejects bad arguments on the host before enqueueing anything."""
+import ctypes
+
+import pytest
+
+import expert_routed_ffn_amd as m
+from expert_routed_ffn_amd import _lib
+
+L = _lib.lib
+
+
+def test_every_declared_function_is_exported():
+    names = m.header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert m.abi_version() == 1
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(6) == b"MOE_ECAPACITY"
+
+
+def test_expert_bytes_formula():
+    for H, I, b in [(2048, 512, 2), (2048, 512, 4), (64, 32, 2), (96, 64, 4)]:
+        assert m.expert_bytes(H, I, b) % 256 == 0
+        assert m.expert_bytes(H, I, b) >= 3 * H * I * (b / 8 + 4 / 32)
+    assert m.expert_bytes(2048, 512, 2) == 1179648
+    assert m.expert_bytes(2048, 512, 3) == 0  # unsupported width
+
+
+NULL = None
+
+
+def _st(v):
+    return int(v)
+
+
+@pytest.mark.parametrize("E,k,expect", [(0, 1, _lib.MOE_EUNSUPPORTED), (1025, 2, _lib.MOE_EUNSUPPORTED),
+                                        (8, 0, _lib.MOE_EUNSUPPORTED), (8, 17, _lib.MOE_EUNSUPPORTED),
+                                        (4, 5, _lib.MOE_EUNSUPPORTED), (8, 2, _lib.MOE_EINVAL)])
+def test_route_topk_argument_checks(E, k, expect):
+    # T = 3 with null pointers: either the sizes or the pointers are rejected on the host.
+    assert _st(L.moe_route_topk(NULL, 3, E, k, NULL, NULL, NULL)) == expect
+    assert b"moe_route_topk" in L.moe_last_error()
+
+
+def test_route_topk_negative_T():
+    assert _st(L.moe_route_topk(NULL, -1, 8, 2, NULL, NULL, NULL)) == _lib.MOE_EINVAL
+
+
+def test_zero_tokens_is_a_no_op():
+    assert _st(L.moe_route_topk(NULL, 0, 8, 2, NULL, NULL, NULL)) == _lib.MOE_OK
+
+
+def test_dispatch_argument_checks():
+    fake = ctypes.c_void_p(0x1000)
+    assert _st(L.moe_dispatch(NULL, 3, 2, 8, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL)) == _lib.MOE_EINVAL
+    # large n needs a workspace
+    need = int(L.moe_dispatch_workspace_bytes(8192, 10, 512))
+    assert need > 0
+    assert int(L.moe_dispatch_workspace_bytes(3, 10, 512)) == 0
+    st = L.moe_dispatch(fake, 8192, 10, 512, fake, fake, fake, fake, fake, fake, need - 1, NULL)
+    assert _st(st) == _lib.MOE_EWORKSPACE
+
+
+def _q(E=8, H=64, I=32, bits=2, base=0x100, stride=None):
+    return _lib.QLayer(E, H, I, bits, base, stride if stride is not None else m.expert_bytes(H, I, bits), None)
+
+
+def test_expert_ffn_argument_checks():
+    fake = ctypes.c_void_p(0x1000)
+
+    def call(q, T=2, k=2, x_t=1, y_t=0, path=0, ws_bytes=1 << 20, x=fake):
+        return _st(L.moe_expert_ffn_q(ctypes.byref(q), x, x_t, T, k, fake, fake, fake, fake, fake, y_t, path, fake,
+                                      ws_bytes, NULL))
+
+    assert call(_q(bits=3)) == _lib.MOE_EUNSUPPORTED
+    assert call(_q(H=48)) == _lib.MOE_EUNSUPPORTED
+    assert call(_q(I=16)) == _lib.MOE_EUNSUPPORTED
+    assert call(_q(stride=100)) == _lib.MOE_EINVAL
+    assert call(_q(base=0x101)) == _lib.MOE_EINVAL
+    assert call(_q(), x=ctypes.c_void_p(0x1004)) == _lib.MOE_EINVAL
+    assert call(_q(), x_t=7) == _lib.MOE_EINVAL
+    assert call(_q(), path=9) == _lib.MOE_EINVAL
+    assert call(_q(), ws_bytes=0) == _lib.MOE_EWORKSPACE
+    assert call(_q(), T=0) == _lib.MOE_OK
+
+
+def test_combine_argument_checks():
+    fake = ctypes.c_void_p(0x1000)
+    assert _st(L.moe_combine(NULL, 0, NULL, 2, 2, 64, NULL, 0, NULL, NULL, NULL)) == _lib.MOE_EINVAL
+    assert _st(L.moe_combine(fake, 0, fake, 2, 17, 64, NULL, 0, fake, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_combine(fake, 0, fake, 2, 2, 66, NULL, 0, fake, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_combine(fake, 5, fake, 2, 2, 64, NULL, 0, fake, NULL, NULL)) == _lib.MOE_EINVAL
