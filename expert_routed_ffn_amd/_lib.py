@@ -83,6 +83,8 @@ def _load():
     L.moe_slot_table_create_host.argtypes = [i32, i32, i32, COPY_FN, vp, ctypes.POINTER(vp)]
     L.moe_slot_table_resolve_host.restype = st
     L.moe_slot_table_resolve_host.argtypes = [vp, i32, vp, i32]
+    L.moe_profile_next_launch.restype = st
+    L.moe_profile_next_launch.argtypes = [i32, vp, vp]
     return L
 
 
@@ -126,6 +128,16 @@ def _need(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+KERNELS = {"route": 0, "dispatch": 1, "gemv_gateup": 2, "gemv_down": 3, "mfma_gateup": 4, "mfma_down": 5,
+           "combine": 6}
+
+
+def profile_next_launch(kernel: str, start, stop):
+    """Attach HIP events (raw hipEvent_t handles) to the next launch of `kernel` on this thread."""
+    _check(lib.moe_profile_next_launch(KERNELS[kernel], ctypes.c_void_p(int(getattr(start, "value", start))),
+                                       ctypes.c_void_p(int(getattr(stop, "value", stop)))))
 
 
 def abi_version() -> int:

@@ -23,6 +23,11 @@ moe_status check_hip(hipError_t e, const char* what) {
 
 moe_status check_launch(const char* what) { return check_hip(hipGetLastError(), what); }
 
+ProfileReq& profile_req() {
+  static thread_local ProfileReq req;
+  return req;
+}
+
 static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 
 BlobLayout blob_layout(int H, int I, int bits) {
@@ -182,6 +187,16 @@ moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int 
       (out_bf16 && !aligned(out_bf16, 8)))
     return fail(MOE_EINVAL, "moe_combine: misaligned buffer");
   return launch_combine(y, y_t, w, T, k, H, residual, r_t, out, out_bf16, stream);
+}
+
+moe_status moe_profile_next_launch(moe_kernel kernel, hipEvent_t start, hipEvent_t stop) {
+  if ((int)kernel < 0 || (int)kernel > (int)MOE_KERNEL_COMBINE) return fail(MOE_EINVAL, "moe_profile_next_launch: kernel");
+  if (!start || !stop) return fail(MOE_EINVAL, "moe_profile_next_launch: null event");
+  ProfileReq& p = profile_req();
+  p.kernel = (int)kernel;
+  p.start = start;
+  p.stop = stop;
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -62,9 +62,11 @@ void launch_r(const YT* y, const float* w, int T, int k, int H, const void* resi
               uint16_t* out_bf16, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(H / 4, 256), (unsigned)T), block(256);
   if (residual && r_t == MOE_BF16)
-    combine_kernel<YT, uint16_t><<<grid, block, 0, s>>>(y, w, T, k, H, (const uint16_t*)residual, out, out_bf16);
+    launch_k(MOE_KERNEL_COMBINE, combine_kernel<YT, uint16_t>, grid, block, 0, s, y, w, T, k, H,
+             (const uint16_t*)residual, out, out_bf16);
   else
-    combine_kernel<YT, float><<<grid, block, 0, s>>>(y, w, T, k, H, (const float*)residual, out, out_bf16);
+    launch_k(MOE_KERNEL_COMBINE, combine_kernel<YT, float>, grid, block, 0, s, y, w, T, k, H,
+             (const float*)residual, out, out_bf16);
 }
 
 }  // namespace

@@ -208,17 +208,18 @@ size_t dispatch_ws_bytes(int n, int E) {
 moe_status launch_dispatch(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* sorted_assign,
                            int32_t* assign_pos, int32_t* active, int32_t* n_active, void* ws, hipStream_t s) {
   if (n == 0) {
-    dispatch_empty_kernel<<<1, 256, 0, s>>>(E, offsets, n_active);
+    launch_k(MOE_KERNEL_DISPATCH, dispatch_empty_kernel, dim3(1), dim3(256), 0, s, E, offsets, n_active);
     return check_launch("dispatch_empty");
   }
   if (n <= kSmallN) {
-    dispatch_small_kernel<<<1, kBlock, 0, s>>>(ids, n, E, offsets, sorted_assign, assign_pos, active, n_active);
+    launch_k(MOE_KERNEL_DISPATCH, dispatch_small_kernel, dim3(1), dim3(kBlock), 0, s, ids, n, E, offsets,
+             sorted_assign, assign_pos, active, n_active);
     return check_launch("dispatch_small");
   }
   const int nchunks = (int)ceil_div(n, kBlock);
   int32_t* rank = (int32_t*)ws;
   int32_t* chunk = rank + ((n + 63) / 64) * 64;
-  dispatch_rank_kernel<<<nchunks, kBlock, 0, s>>>(ids, n, E, rank, chunk);
+  launch_k(MOE_KERNEL_DISPATCH, dispatch_rank_kernel, dim3(nchunks), dim3(kBlock), 0, s, ids, n, E, rank, chunk);
   if (moe_status st = check_launch("dispatch_rank")) return st;
   dispatch_scan_kernel<<<1, kBlock, 0, s>>>(nchunks, E, chunk, offsets, active, n_active);
   if (moe_status st = check_launch("dispatch_scan")) return st;

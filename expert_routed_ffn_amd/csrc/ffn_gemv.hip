@@ -418,14 +418,10 @@ moe_status launch_bits_tm(const moe_qlayer& q, const BlobLayout& L, const void* 
     const int NI = RL * RPI / 2;
     const int tiles = (int)ceil_div(q.I, 4 * NI);
     const dim3 grid((unsigned)(max_active * tiles)), block(256);
-    if (split)
-      ffn_gateup_kernel<BITS, TM, true, kRLGateUpSplit<TM>><<<grid, block, 0, s>>>(
-          base, q.stride, q.slot_map, q.H, q.I, L.gate_codes, L.gate_sm, L.up_codes, L.up_sm, x, offsets,
-          sorted_assign, active, n_active, k, tiles, geo, h_ws);
-    else
-      ffn_gateup_kernel<BITS, TM, false, kRLGateUp<TM>><<<grid, block, 0, s>>>(
-          base, q.stride, q.slot_map, q.H, q.I, L.gate_codes, L.gate_sm, L.up_codes, L.up_sm, x, offsets,
-          sorted_assign, active, n_active, k, tiles, geo, h_ws);
+    const auto kern = split ? ffn_gateup_kernel<BITS, TM, true, kRLGateUpSplit<TM>>
+                            : ffn_gateup_kernel<BITS, TM, false, kRLGateUp<TM>>;
+    launch_k(MOE_KERNEL_GEMV_GATEUP, kern, grid, block, 0, s, base, q.stride, q.slot_map, q.H, q.I, L.gate_codes,
+             L.gate_sm, L.up_codes, L.up_sm, x, offsets, sorted_assign, active, n_active, k, tiles, geo, h_ws);
     if (moe_status st = check_launch("ffn_gateup")) return st;
   }
   // kernel 2
@@ -436,14 +432,9 @@ moe_status launch_bits_tm(const moe_qlayer& q, const BlobLayout& L, const void* 
     const int RPI = 64 / geo.G;
     const int tiles = (int)ceil_div(q.H, 4 * kRLDown<TM> * RPI);
     const dim3 grid((unsigned)(max_active * tiles)), block(256);
-    if (ybf16)
-      ffn_down_kernel<BITS, TM, kRLDown<TM>, true><<<grid, block, 0, s>>>(base, q.stride, q.slot_map, q.H, q.I,
-                                                                      L.down_codes, L.down_sm, h_ws, offsets,
-                                                                      sorted_assign, active, n_active, tiles, geo, y);
-    else
-      ffn_down_kernel<BITS, TM, kRLDown<TM>, false><<<grid, block, 0, s>>>(base, q.stride, q.slot_map, q.H, q.I,
-                                                                       L.down_codes, L.down_sm, h_ws, offsets,
-                                                                       sorted_assign, active, n_active, tiles, geo, y);
+    const auto kern = ybf16 ? ffn_down_kernel<BITS, TM, kRLDown<TM>, true> : ffn_down_kernel<BITS, TM, kRLDown<TM>, false>;
+    launch_k(MOE_KERNEL_GEMV_DOWN, kern, grid, block, 0, s, base, q.stride, q.slot_map, q.H, q.I, L.down_codes,
+             L.down_sm, h_ws, offsets, sorted_assign, active, n_active, tiles, geo, y);
     return check_launch("ffn_down");
   }
 }

@@ -2,6 +2,7 @@
 // Nothing here is part of the C ABI (that is include/moe.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -50,6 +51,26 @@ moe_status launch_combine(const void* y, moe_dtype y_t, const float* w, int T, i
                           moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t s);
 
 moe_status launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// Pending timing request of moe_profile_next_launch (per host thread).
+struct ProfileReq {
+  int kernel = -1;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfileReq& profile_req();
+
+// Launches `kernel`; when a timing request for kernel id `kid` is pending, the
+// launch goes through hipExtLaunchKernelGGL with the requested events.
+template <typename F, typename... Args>
+inline void launch_k(int kid, F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  ProfileReq& p = profile_req();
+  if (p.kernel == kid) {
+    p.kernel = -1;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, p.start, p.stop, 0, args...);
+  } else {
+    kernel<<<grid, block, shmem, s>>>(args...);
+  }
+}
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -88,16 +88,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 moe_status launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
   const int epl = (int)ceil_div(E, 64);
-  if (epl <= 1)
-    route_topk_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else if (epl <= 2)
-    route_topk_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else if (epl <= 4)
-    route_topk_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else if (epl <= 8)
-    route_topk_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
-  else
-    route_topk_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  const auto kern = epl <= 1   ? route_topk_kernel<1>
+                    : epl <= 2 ? route_topk_kernel<2>
+                    : epl <= 4 ? route_topk_kernel<4>
+                    : epl <= 8 ? route_topk_kernel<8>
+                               : route_topk_kernel<16>;
+  launch_k(MOE_KERNEL_ROUTE, kern, grid, block, 0, s, logits, T, E, k, ids, w);
   return check_launch("route_topk");
 }
 

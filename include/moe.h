@@ -224,6 +224,24 @@ moe_status moe_slot_table_map_host(const moe_slot_table* t, int32_t* out);
 void moe_slot_table_destroy(moe_slot_table* t);
 
 /*
+ * Kernel timing hook (for measurement tools; not part of the layer).  The
+ * next launch of `kernel` issued by this host thread is made with
+ * hipExtLaunchKernel so that `start` and `stop` (created by the caller with
+ * hipEventCreate) record the start and end of that kernel's execution on its
+ * stream.  One request is pending at a time; a new call replaces it.
+ */
+typedef enum moe_kernel {
+  MOE_KERNEL_ROUTE = 0,
+  MOE_KERNEL_DISPATCH = 1,
+  MOE_KERNEL_GEMV_GATEUP = 2,
+  MOE_KERNEL_GEMV_DOWN = 3,
+  MOE_KERNEL_MFMA_GATEUP = 4,
+  MOE_KERNEL_MFMA_DOWN = 5,
+  MOE_KERNEL_COMBINE = 6
+} moe_kernel;
+moe_status moe_profile_next_launch(moe_kernel kernel, hipEvent_t start, hipEvent_t stop);
+
+/*
  * Host-only slot table for exercising the policy without a GPU.  Every copy
  * the real table would enqueue is reported to copy_fn(user, slot, layer,
  * expert) instead; resolve takes a host array of active experts.
