@@ -1,17 +1,292 @@
 // slot_table.hip -- resident-expert slot table (host side).
+//
+// Strata feature (tech.hub77a.com), section "2. 왜 대단한가" (2): the most-called
+// experts stay resident in GPU memory and all of them sit in host RAM; a
+// routed expert that is resident is used at once, any other is first moved in
+// from RAM.  Janas-LLM item (onedev.kr/items/2196): experts that come back are
+// kept cached.  Strata feature, section "3. 바로 써먹기": part of host memory is
+// locked for the graphics card at load time.
+//
+// The table owns the placement of L*E (layer, expert) blobs in n_slots device
+// slots.  The policy is least-recently-used over (layer, expert), kept as an
+// index-linked list of slots (head = least recently used).  A resolve first
+// marks every hit as most recently used, then serves the misses in ascending
+// expert id, each taking the list head as victim; since every slot used by the
+// current resolve has just moved to the tail, a victim is never one of them
+// (n_active <= n_slots is checked first).
+//
+// Copies go straight from the page-locked master copy into the victim slot
+// with hipMemcpyAsync on the caller's stream, so the FFN kernels enqueued after
+// the resolve see them.  The device map is re-uploaded from a page-locked
+// mirror; a resolve waits for the stream before touching the mirror, so the
+// previous upload has always completed before the mirror is modified (no
+// staging buffer is reused while a copy from it may be in flight).
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
 #include "internal.hpp"
 
+struct moe_slot_table {
+  int L = 0, E = 0, n_slots = 0;
+  size_t expert_bytes = 0;
+  bool host_only = false;
+  // device mode
+  const uint8_t* host = nullptr;  // page-locked master copy [L*E*expert_bytes]
+  uint8_t* slots = nullptr;       // device [n_slots*expert_bytes]
+  int32_t* slot_map_dev = nullptr;
+  int32_t* map_mirror = nullptr;  // page-locked [L*E]
+  int32_t* act_stage = nullptr;   // page-locked [E + 1]
+  // host-only mode
+  moe_copy_fn copy_fn = nullptr;
+  void* user = nullptr;
+  // policy state
+  std::vector<int32_t> map;    // [L*E] slot or -1
+  std::vector<int32_t> owner;  // [n_slots] l*E + e or -1
+  std::vector<int32_t> prev, next;
+  int32_t head = -1, tail = -1;
+  moe_slot_stats stats{};
+};
+
+namespace {
+
+using moe::fail;
+
+void lru_unlink(moe_slot_table* t, int s) {
+  const int p = t->prev[s], n = t->next[s];
+  if (p >= 0) t->next[p] = n; else t->head = n;
+  if (n >= 0) t->prev[n] = p; else t->tail = p;
+  t->prev[s] = t->next[s] = -1;
+}
+
+void lru_push_tail(moe_slot_table* t, int s) {
+  t->prev[s] = t->tail;
+  t->next[s] = -1;
+  if (t->tail >= 0) t->next[t->tail] = s; else t->head = s;
+  t->tail = s;
+}
+
+void lru_touch(moe_slot_table* t, int s) {
+  if (t->tail == s) return;
+  lru_unlink(t, s);
+  lru_push_tail(t, s);
+}
+
+void init_policy(moe_slot_table* t) {
+  t->map.assign((size_t)t->L * t->E, -1);
+  t->owner.assign(t->n_slots, -1);
+  t->prev.assign(t->n_slots, -1);
+  t->next.assign(t->n_slots, -1);
+  t->head = t->tail = -1;
+  for (int s = 0; s < t->n_slots; ++s) lru_push_tail(t, s);  // free slots are used in ascending order
+}
+
+// Place (layer, expert) into the LRU victim slot; returns the slot.
+int place(moe_slot_table* t, int layer, int expert) {
+  const int s = t->head;
+  const int64_t idx = (int64_t)layer * t->E + expert;
+  if (t->owner[s] >= 0) {
+    t->map[t->owner[s]] = -1;
+    t->stats.evictions++;
+  }
+  t->owner[s] = (int32_t)idx;
+  t->map[idx] = s;
+  lru_touch(t, s);
+  return s;
+}
+
+moe_status do_copy(moe_slot_table* t, int slot, int layer, int expert, hipStream_t stream) {
+  t->stats.bytes_h2d += t->expert_bytes;
+  if (t->host_only) {
+    t->copy_fn(t->user, slot, layer, expert);
+    return MOE_OK;
+  }
+  const uint8_t* src = t->host + ((size_t)layer * t->E + expert) * t->expert_bytes;
+  uint8_t* dst = t->slots + (size_t)slot * t->expert_bytes;
+  return moe::check_hip(hipMemcpyAsync(dst, src, t->expert_bytes, hipMemcpyHostToDevice, stream),
+                        "slot table: expert copy");
+}
+
+moe_status upload_map(moe_slot_table* t, hipStream_t stream) {
+  if (t->host_only) return MOE_OK;
+  std::memcpy(t->map_mirror, t->map.data(), t->map.size() * sizeof(int32_t));
+  return moe::check_hip(hipMemcpyAsync(t->slot_map_dev, t->map_mirror, t->map.size() * sizeof(int32_t),
+                                       hipMemcpyHostToDevice, stream),
+                        "slot table: map upload");
+}
+
+// The policy step shared by the device and host-only tables.
+moe_status resolve_list(moe_slot_table* t, int layer, const int32_t* act, int n, hipStream_t stream, bool& changed) {
+  changed = false;
+  if (n > t->n_slots)
+    return fail(MOE_ECAPACITY, "moe_slot_table_resolve: " + std::to_string(n) + " active experts, " +
+                                   std::to_string(t->n_slots) + " slots");
+  for (int i = 0; i < n; ++i)
+    if (act[i] < 0 || act[i] >= t->E) return fail(MOE_EINVAL, "moe_slot_table_resolve: expert id out of range");
+  t->stats.resolves++;
+  std::vector<int32_t> misses;
+  for (int i = 0; i < n; ++i) {
+    const int64_t idx = (int64_t)layer * t->E + act[i];
+    const int s = t->map[idx];
+    if (s >= 0) {
+      t->stats.hits++;
+      lru_touch(t, s);
+    } else {
+      misses.push_back(act[i]);
+    }
+  }
+  std::sort(misses.begin(), misses.end());
+  misses.erase(std::unique(misses.begin(), misses.end()), misses.end());
+  for (int e : misses) {
+    t->stats.misses++;
+    const int s = place(t, layer, e);
+    if (moe_status st = do_copy(t, s, layer, e, stream)) return st;
+    changed = true;
+  }
+  return MOE_OK;
+}
+
+void free_table(moe_slot_table* t) {
+  if (!t) return;
+  if (t->map_mirror) (void)hipHostFree(t->map_mirror);
+  if (t->act_stage) (void)hipHostFree(t->act_stage);
+  delete t;
+}
+
+}  // namespace
+
 extern "C" {
-moe_status moe_slot_table_create(int, int, int, size_t, const void*, void*, int32_t*, hipStream_t, moe_slot_table**) {
-  return moe::fail(MOE_EUNSUPPORTED, "slot table not available in this build");
+
+moe_status moe_slot_table_create(int L, int E, int n_slots, size_t expert_bytes, const void* host_experts, void* slots,
+                                 int32_t* slot_map, hipStream_t stream, moe_slot_table** out) {
+  if (!out) return fail(MOE_EINVAL, "moe_slot_table_create: null out");
+  *out = nullptr;
+  if (L < 1 || E < 1 || E > moe::kMaxE || n_slots < 1)
+    return fail(MOE_EINVAL, "moe_slot_table_create: L, E or n_slots out of range");
+  if (expert_bytes == 0 || expert_bytes % 256)
+    return fail(MOE_EINVAL, "moe_slot_table_create: expert_bytes must be a nonzero multiple of 256");
+  if (!host_experts || !slots || !slot_map) return fail(MOE_EINVAL, "moe_slot_table_create: null pointer");
+  hipPointerAttribute_t attr;
+  const hipError_t pe = hipPointerGetAttributes(&attr, host_experts);
+  if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(MOE_ENOTPINNED, "moe_slot_table_create: host_experts is not page-locked host memory");
+  }
+  moe_slot_table* t = new moe_slot_table;
+  t->L = L;
+  t->E = E;
+  t->n_slots = n_slots;
+  t->expert_bytes = expert_bytes;
+  t->host = static_cast<const uint8_t*>(host_experts);
+  t->slots = static_cast<uint8_t*>(slots);
+  t->slot_map_dev = slot_map;
+  if (hipHostMalloc((void**)&t->map_mirror, sizeof(int32_t) * (size_t)L * E, hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&t->act_stage, sizeof(int32_t) * ((size_t)E + 1), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    free_table(t);
+    return fail(MOE_EHIP, "moe_slot_table_create: page-locked staging allocation failed");
+  }
+  init_policy(t);
+  if (moe_status st = upload_map(t, stream)) {
+    free_table(t);
+    return st;
+  }
+  *out = t;
+  return MOE_OK;
 }
-moe_status moe_slot_table_preload(moe_slot_table*, const int32_t*, int, hipStream_t) { return MOE_EUNSUPPORTED; }
-moe_status moe_slot_table_resolve(moe_slot_table*, int, const int32_t*, const int32_t*, hipStream_t) {
-  return MOE_EUNSUPPORTED;
+
+moe_status moe_slot_table_create_host(int L, int E, int n_slots, moe_copy_fn copy_fn, void* user,
+                                      moe_slot_table** out) {
+  if (!out) return fail(MOE_EINVAL, "moe_slot_table_create_host: null out");
+  *out = nullptr;
+  if (L < 1 || E < 1 || E > moe::kMaxE || n_slots < 1)
+    return fail(MOE_EINVAL, "moe_slot_table_create_host: L, E or n_slots out of range");
+  if (!copy_fn) return fail(MOE_EINVAL, "moe_slot_table_create_host: null copy_fn");
+  moe_slot_table* t = new moe_slot_table;
+  t->L = L;
+  t->E = E;
+  t->n_slots = n_slots;
+  t->expert_bytes = 256;
+  t->host_only = true;
+  t->copy_fn = copy_fn;
+  t->user = user;
+  init_policy(t);
+  *out = t;
+  return MOE_OK;
 }
-moe_status moe_slot_table_stats(const moe_slot_table*, moe_slot_stats*) { return MOE_EUNSUPPORTED; }
-moe_status moe_slot_table_map_host(const moe_slot_table*, int32_t*) { return MOE_EUNSUPPORTED; }
-void moe_slot_table_destroy(moe_slot_table*) {}
-moe_status moe_slot_table_create_host(int, int, int, moe_copy_fn, void*, moe_slot_table**) { return MOE_EUNSUPPORTED; }
-moe_status moe_slot_table_resolve_host(moe_slot_table*, int, const int32_t*, int) { return MOE_EUNSUPPORTED; }
+
+moe_status moe_slot_table_preload(moe_slot_table* t, const int32_t* layer_expert, int n, hipStream_t stream) {
+  if (!t) return fail(MOE_EINVAL, "moe_slot_table_preload: null table");
+  if (n < 0 || (n > 0 && !layer_expert)) return fail(MOE_EINVAL, "moe_slot_table_preload: bad list");
+  for (int i = 0; i < n; ++i) {
+    const int l = layer_expert[2 * i], e = layer_expert[2 * i + 1];
+    if (l < 0 || l >= t->L || e < 0 || e >= t->E) return fail(MOE_EINVAL, "moe_slot_table_preload: pair out of range");
+  }
+  if (!t->host_only) {
+    // the mirror and slots may still be read by earlier work on the stream
+    if (moe_status st = moe::check_hip(hipStreamSynchronize(stream), "moe_slot_table_preload: sync")) return st;
+  }
+  bool changed = false;
+  for (int i = 0; i < n; ++i) {
+    const int l = layer_expert[2 * i], e = layer_expert[2 * i + 1];
+    const int64_t idx = (int64_t)l * t->E + e;
+    if (t->map[idx] >= 0) {
+      lru_touch(t, t->map[idx]);
+      continue;
+    }
+    const int s = place(t, l, e);
+    if (moe_status st = do_copy(t, s, l, e, stream)) return st;
+    changed = true;
+  }
+  return changed ? upload_map(t, stream) : MOE_OK;
 }
+
+moe_status moe_slot_table_resolve(moe_slot_table* t, int layer, const int32_t* active, const int32_t* n_active,
+                                  hipStream_t stream) {
+  if (!t || t->host_only) return fail(MOE_EINVAL, "moe_slot_table_resolve: not a device table");
+  if (layer < 0 || layer >= t->L) return fail(MOE_EINVAL, "moe_slot_table_resolve: layer out of range");
+  if (!active || !n_active) return fail(MOE_EINVAL, "moe_slot_table_resolve: null pointer");
+  // 1) how many experts are active (waits for the routing work queued before us)
+  if (moe_status st = moe::check_hip(hipMemcpyAsync(t->act_stage, n_active, sizeof(int32_t), hipMemcpyDeviceToHost,
+                                                    stream), "moe_slot_table_resolve: copy n_active"))
+    return st;
+  if (moe_status st = moe::check_hip(hipStreamSynchronize(stream), "moe_slot_table_resolve: sync")) return st;
+  const int n = t->act_stage[0];
+  if (n < 0 || n > t->E) return fail(MOE_EINVAL, "moe_slot_table_resolve: n_active out of range");
+  // 2) which
+  if (n > 0) {
+    if (moe_status st = moe::check_hip(hipMemcpyAsync(t->act_stage + 1, active, sizeof(int32_t) * (size_t)n,
+                                                      hipMemcpyDeviceToHost, stream),
+                                       "moe_slot_table_resolve: copy active"))
+      return st;
+    if (moe_status st = moe::check_hip(hipStreamSynchronize(stream), "moe_slot_table_resolve: sync")) return st;
+  }
+  bool changed = false;
+  if (moe_status st = resolve_list(t, layer, t->act_stage + 1, n, stream, changed)) return st;
+  return changed ? upload_map(t, stream) : MOE_OK;
+}
+
+moe_status moe_slot_table_resolve_host(moe_slot_table* t, int layer, const int32_t* active, int n_active) {
+  if (!t || !t->host_only) return fail(MOE_EINVAL, "moe_slot_table_resolve_host: not a host-only table");
+  if (layer < 0 || layer >= t->L) return fail(MOE_EINVAL, "moe_slot_table_resolve_host: layer out of range");
+  if (n_active < 0 || (n_active > 0 && !active)) return fail(MOE_EINVAL, "moe_slot_table_resolve_host: bad list");
+  bool changed = false;
+  return resolve_list(t, layer, active, n_active, nullptr, changed);
+}
+
+moe_status moe_slot_table_stats(const moe_slot_table* t, moe_slot_stats* out) {
+  if (!t || !out) return fail(MOE_EINVAL, "moe_slot_table_stats: null pointer");
+  *out = t->stats;
+  return MOE_OK;
+}
+
+moe_status moe_slot_table_map_host(const moe_slot_table* t, int32_t* out) {
+  if (!t || !out) return fail(MOE_EINVAL, "moe_slot_table_map_host: null pointer");
+  std::memcpy(out, t->map.data(), t->map.size() * sizeof(int32_t));
+  return MOE_OK;
+}
+
+void moe_slot_table_destroy(moe_slot_table* t) { free_table(t); }
+
+}  // extern "C"

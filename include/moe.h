@@ -204,8 +204,9 @@ moe_status moe_slot_table_create(int L, int E, int n_slots, size_t expert_bytes,
                                  int32_t* slot_map, hipStream_t stream, moe_slot_table** out);
 
 /* Make the given (layer, expert) pairs resident (host array of 2*n int32:
- * layer, expert, ...), in order, evicting least recently used slots.  Copies
- * are enqueued on stream; the call returns after enqueueing. */
+ * layer, expert, ...), in order, evicting least recently used slots.  Waits
+ * for earlier work on stream (the slots and the map may still be in use),
+ * then enqueues the copies and the map update on stream. */
 moe_status moe_slot_table_preload(moe_slot_table* t, const int32_t* layer_expert, int n, hipStream_t stream);
 
 /* Make every expert in active[0 .. *n_active) of `layer` resident.  active and

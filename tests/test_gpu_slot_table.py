@@ -1,0 +1,137 @@
+"""GPU: the resident-expert slot table changes placement only, never results.
+
+A small chained stack (layers feed each other through combine's residual and
+bf16 output) runs once with every expert resident in device memory and once
+through a slot table holding only part of them, misses copied from
+page-locked host memory; every layer's outputs must be bit-identical.  The
+stack's first layer is also checked against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._parity import row_rel_err, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import expert_routed_ffn_amd as m
+    return m
+
+
+def _stack(L=4, E=64, H=256, I=128, bits=2, T=3, k=6):
+    return synth.Workload("small_stack", E=E, k=k, H=H, I=I, T=T, bits=bits, x_dtype="bf16", zipf_s=1.2, layers=L)
+
+
+def _host_master(w, torch):
+    eb = w.expert_bytes
+    host = torch.empty(w.layers * w.E * eb, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy().reshape(w.layers, w.E, eb)
+    for l in range(w.layers):
+        synth.layer_experts(w.seed, l, w.E, w.H, w.I, w.bits, out=hv[l])
+    return host
+
+
+def _run(moe, torch, w, layer_of, steps, resolve=None):
+    """Run `steps` decode steps through the stack; returns every layer's (y, out) per step."""
+    dev = torch.device("cuda")
+    outs = []
+    for s in range(steps):
+        x = torch.from_numpy(w.x(0, s).view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        for l in range(w.layers):
+            lg_np = synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, l, s), w.T, w.E,
+                                 synth.drifted_bias(w, l, s, 0.05))
+            lg = torch.from_numpy(lg_np).to(dev)
+            ids, wt = moe.route_topk(lg, w.k)
+            d = moe.dispatch(ids, w.E)
+            if resolve is not None:
+                resolve(l, d)
+            y = moe.expert_ffn_q(layer_of(l), x, w.k, d, path="gemv")
+            nxt = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+            out = moe.combine(y, wt, residual=x, out_bf16=nxt.view(torch.int16))
+            torch.cuda.synchronize()
+            outs.append((to_host(y).copy(), to_host(out).copy()))
+            x = nxt
+    return outs
+
+
+@pytest.mark.parametrize("n_slots", [64, 24])
+def test_slot_table_matches_resident_bit_for_bit(moe, n_slots):
+    import torch
+    w = _stack()
+    eb = w.expert_bytes
+    host = _host_master(w, torch)
+    dev_all = host.to("cuda")
+    resident = [moe.ExpertLayer(w.E, w.H, w.I, w.bits, dev_all, eb, base_offset=l * w.E * eb) for l in range(w.layers)]
+    ref = _run(moe, torch, w, lambda l: resident[l], steps=4)
+
+    slots = torch.empty(n_slots * eb, dtype=torch.uint8, device="cuda")
+    smap = torch.empty(w.layers * w.E, dtype=torch.int32, device="cuda")
+    table = moe.SlotTable(w.layers, w.E, n_slots, eb, host, slots, smap)
+    # warm start: the most popular experts of each layer by the step-0 bias
+    pairs = []
+    for l in range(w.layers):
+        order = np.argsort(-w.bias(l), kind="stable")[: n_slots // (2 * w.layers)]
+        pairs += [(l, int(e)) for e in order]
+    table.preload(pairs)
+    got = _run(moe, torch, w, lambda l: table.layer(l, w.H, w.I, w.bits), steps=4,
+               resolve=lambda l, d: table.resolve(l, d))
+    st = table.stats()
+    table.close()
+    assert st["misses"] > 0 and st["resolves"] == 4 * w.layers
+    if n_slots < 64:
+        assert st["evictions"] > 0
+    for (ya, oa), (yb, ob) in zip(ref, got):
+        assert np.array_equal(ya, yb) and np.array_equal(oa, ob)
+
+
+def test_stack_first_layer_matches_oracle(moe):
+    import torch
+    w = _stack()
+    host = _host_master(w, torch)
+    eb = w.expert_bytes
+    dev_all = host.to("cuda")
+    layer0 = moe.ExpertLayer(w.E, w.H, w.I, w.bits, dev_all, eb)
+    lg_np = synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, 0, 0), w.T, w.E, synth.drifted_bias(w, 0, 0, 0.05))
+    x_np = w.x(0, 0)
+    x = torch.from_numpy(x_np.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    ids, wt, d, y, out = moe.layer_forward(layer0, x, to_dev(lg_np), w.k, residual=x, path="gemv")
+    ex = host.numpy().reshape(w.layers, w.E, eb)[0]
+    res = (x_np.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = oracle.layer(x_np, lg_np, ex, w.k, w.H, w.I, w.bits, residual=res)
+    assert np.array_equal(to_host(ids), ref["ids"])
+    assert row_rel_err(to_host(out) - res, ref["out"] - res) <= 2e-3
+
+
+def test_slot_table_rejects_pageable_host_memory(moe):
+    import torch
+    w = _stack(L=1, E=8, H=64, I=32)
+    eb = w.expert_bytes
+    host = torch.empty(w.E * eb, dtype=torch.uint8)  # pageable
+    slots = torch.empty(4 * eb, dtype=torch.uint8, device="cuda")
+    smap = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.SlotTable(1, w.E, 4, eb, host, slots, smap)
+    assert ei.value.status == 5  # MOE_ENOTPINNED
+
+
+def test_slot_table_capacity_error(moe):
+    import torch
+    w = _stack(L=1, E=16, H=64, I=32, T=3, k=4)
+    eb = w.expert_bytes
+    host = _host_master(w, torch)
+    slots = torch.empty(2 * eb, dtype=torch.uint8, device="cuda")
+    smap = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    table = moe.SlotTable(1, w.E, 2, eb, host, slots, smap)
+    ids = torch.tensor([[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11]], dtype=torch.int32, device="cuda")
+    d = moe.dispatch(ids, w.E)
+    with pytest.raises(moe.MoeError) as ei:
+        table.resolve(0, d)
+    assert ei.value.status == 6  # MOE_ECAPACITY
+    table.close()
