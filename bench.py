@@ -20,7 +20,9 @@ The JSON line also carries:
                 to that kernel's own launch (moe_profile_next_launch);
   cpu_baseline  the CPU oracle (scalar C, fp64, one thread) on a bounded
                 sample of the same layer steps;
-  prefill       (with --prefill) the 8,192-token prompt-chunk layer.
+  prefill       the 8,192-token prompt-chunk layer on the MFMA path (tokens/s,
+                and the gate/up GEMM against the 2.5 PFLOP/s dense half-precision
+                MFMA peak); --no-prefill skips it.
 """
 from __future__ import annotations
 
@@ -180,6 +182,89 @@ def decode_bench(args, torch, moe, synth, oracle):
     return res, (x_np, lg_np, ex, w)
 
 
+def prefill_bench(args, torch, moe, synth, oracle):
+    """8,192-token prompt chunk through one layer (MFMA path)."""
+    import numpy as np
+
+    w = synth.prefill(args.prefill_bias)
+    dev = torch.device("cuda:0")
+    ex = w.experts(nthreads=synth.default_threads())
+    x_np, lg_np = w.x(), w.logits()
+    base = torch.from_numpy(ex.reshape(-1)).to(dev)
+    layer = moe.ExpertLayer(w.E, w.H, w.I, w.bits, base)
+    x = torch.from_numpy(x_np.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    lg = torch.from_numpy(lg_np).to(dev)
+    T, k = w.T, w.k
+    bufs = {
+        "ids": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "dispatch": moe.Dispatch(T, k, w.E, dev),
+        "y": torch.empty((T, k, w.H), dtype=torch.bfloat16, device=dev),
+        "ws": torch.empty(layer.workspace_bytes(T, k, "mfma"), dtype=torch.uint8, device=dev),
+        "out": torch.empty((T, w.H), dtype=torch.float32, device=dev),
+    }
+
+    def step():
+        moe.layer_forward(layer, x, lg, k, bufs=bufs, path="mfma", y_dtype=torch.bfloat16)
+
+    step()
+    torch.cuda.synchronize()
+    sample = np.array([0, 1, T // 2, T - 1])
+    ref = oracle.layer(x_np[sample], lg_np[sample], ex, k, w.H, w.I, w.bits, want_y=False)
+    got = bufs["out"].cpu().numpy()[sample].astype(np.float64)
+    err = float((np.abs(got - ref["out"]).max(axis=1) / np.abs(ref["out"]).max(axis=1)).max())
+    if err > 5e-3:
+        raise SystemExit(f"bench: prefill output does not match the oracle (row error {err:.3e})")
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_steps):
+        step()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / args.prefill_steps
+
+    n = T * k
+    timer = KernelTimer(2 * args.prefill_steps)
+    for i in range(args.prefill_steps):
+        timer.arm(2 * i, "mfma_gateup")
+        moe.expert_ffn_q(layer, x, k, bufs["dispatch"], bufs["y"], path="mfma", ws=bufs["ws"])
+        timer.arm(2 * i + 1, "mfma_down")
+        moe.expert_ffn_q(layer, x, k, bufs["dispatch"], bufs["y"], path="mfma", ws=bufs["ws"])
+    torch.cuda.synchronize()
+    kt = timer.times_ms()
+    timer.close()
+    gu_ms = sum(kt[0::2]) / len(kt[0::2])
+    dn_ms = sum(kt[1::2]) / len(kt[1::2])
+    gu_flops = 2.0 * n * w.H * 2 * w.I
+    dn_flops = 2.0 * n * w.I * w.H
+    counts = np.bincount(bufs["ids"].cpu().numpy().reshape(-1), minlength=w.E)
+    return {
+        "workload": f"prefill chunk: T=8192, 512 experts, top-10, hidden 2048, intermediate 512, 2-bit, "
+                    f"Zipf({1.1 * args.prefill_bias:g}) router bias",
+        "value": T / el,
+        "unit": "tokens/s",
+        "ms_per_step": el * 1e3,
+        "layer_tflops": (gu_flops + dn_flops) / el / 1e12,
+        "experts_hit": int((counts > 0).sum()),
+        "max_rows_per_expert": int(counts.max()),
+        "sample_row_err": err,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": gu_flops / (gu_ms * 1e-3) / 1e12,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "kernel": "mfma_ffn_kernel gate/up (fp16 MFMA, weights decoded in LDS)",
+            "flops_per_launch": gu_flops,
+            "mean_us": gu_ms * 1e3,
+            "down_mean_us": dn_ms * 1e3,
+            "down_tflops": dn_flops / (dn_ms * 1e-3) / 1e12,
+        },
+    }
+
+
 def cpu_baseline(args, oracle, data):
     x_np, lg_np, ex, w = data
     n = args.cpu_steps
@@ -200,6 +285,9 @@ def main():
     ap.add_argument("--copies", type=int, default=48)
     ap.add_argument("--cpu-steps", type=int, default=12)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-bias", type=float, default=1.0, help="scale of the Zipf(1.1) router bias")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -218,6 +306,7 @@ def main():
         sys.exit(1)
 
     res, data = decode_bench(args, torch, moe, synth, oracle)
+    pre = None if args.no_prefill else prefill_bench(args, torch, moe, synth, oracle)
     cpu = None if args.no_cpu else cpu_baseline(args, oracle, data)
     out = {
         "metric": METRIC,
@@ -241,6 +330,7 @@ def main():
         },
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
+        "prefill": pre,
     }
     print(json.dumps(out), flush=True)
 

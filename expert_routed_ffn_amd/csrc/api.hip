@@ -139,7 +139,7 @@ size_t moe_expert_ffn_workspace_bytes(const moe_qlayer* q, int T, int k, moe_ffn
   if (!q || T < 0 || k < 1) return 0;
   const int n = T * k;
   if (resolve_path(path, T) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(n, q->I);
-  return ffn_mfma_ws_bytes(n, q->E, q->I);
+  return ffn_mfma_ws_bytes(T, k, q->E, q->H, q->I);
 }
 
 moe_status moe_expert_ffn_q(const moe_qlayer* q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,

@@ -1,13 +1,462 @@
-// ffn_mfma.hip -- expert FFN for prefill chunks (grouped bf16 MFMA GEMM).
+// ffn_mfma.hip -- expert FFN for prefill chunks: grouped GEMM on bf16 MFMA.
+//
+// Passage: the prompt path reads up to 8,192 tokens per chunk (Strata feature,
+// tech.hub77a.com, section "2. 왜 대단한가" (3)); reading a prompt touches all
+// of the model's parameters (section "4. 해외 반응 쟁점"), so every expert gets
+// many rows and the products become GEMMs.
+//
+// Per active expert e with n_e routed rows (sorted positions p0 .. p0+n_e):
+//   gate/up:  C = X_e [n_e x H] * [Wg; Wu]^T  ->  h = silu(C_g) * C_u  (bf16)
+//   down:     y = h [n_e x I] * Wd^T          ->  scattered to assignment rows
+// Weights are decoded to half precision once per (tile, K-step) into LDS and
+// fed to v_mfma_f32_16x16x32_f16 with fp32 accumulation.  One MFMA's K = 32 is
+// one quantization block, so every K-step decodes one block per weight row.
+//
+// Rounding points: decoded weight = fp16_rne(fp32 fma(s, q, m)); x is
+// converted to fp16 once by a pre-pass (values beyond the fp16 range saturate
+// to +-65504); h = silu(g) * u is rounded to fp16 (saturating); products
+// accumulate in fp32.  The operands are fp16 rather than bf16 because the
+// weights' scale and min are fp16 values: fp16 keeps a decoded weight within
+// 2^-12 of its exact value, bf16 only within 2^-9, and the bf16 rounding of the
+// weights alone already moves outputs by 4e-3 to 9e-3 of their row maximum.
+// Both types run at the same MFMA rate on gfx950.
+//
+// Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x 128 output tile;
+// each wave owns (BM/2) x 64 = (BM/32) x 4 fragments of 16 x 16.  K-steps of
+// 32 go through double-buffered LDS tiles with a 80-byte row pitch (16 lanes
+// reading 16 rows at one column offset hit distinct banks) and one barrier per
+// step.  For gate/up the 128 tile columns are 8 groups of 16: columns 0-7 of a
+// group are gate rows i0+8g .. i0+8g+7 and columns 8-15 the up rows of the same
+// i, so in the MFMA output layout (lane = column) gate and up of one i sit in
+// lanes l and l^8 and SwiGLU needs one lane swap.
+//
+// 2-bit decode uses a 4-entry fp16 table per (row, block): the packed pair of
+// codes (c_even, c_odd) in the two halfwords becomes a v_perm_b32 byte selector
+// (2c, 2c+1 per halfword), i.e. ~2 VALU ops per weight; 4-bit decodes with
+// fp32 fma per weight.
+//
+// A small prep kernel turns (n_active, active, offsets) into the list of
+// (expert slot, first row) M-tiles; the GEMM grid is sized for the worst case
+// and blocks past the list's end exit at once.
 #include "internal.hpp"
 
 namespace moe {
+namespace {
 
-size_t ffn_mfma_ws_bytes(int n_assign, int E, int I) { return (size_t)n_assign * (size_t)I * 2 + (size_t)E * 8 + 4096; }
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-moe_status launch_ffn_mfma(const moe_qlayer&, const void*, moe_dtype, int, int, const int32_t*, const int32_t*,
-                           const int32_t*, const int32_t*, void*, moe_dtype, void*, hipStream_t) {
-  return fail(MOE_EUNSUPPORTED, "moe_expert_ffn_q: the MFMA path is not available in this build");
+constexpr int kBN = 128;
+constexpr int kBK = 32;
+constexpr int kPitch = 40;  // fp16 elements per LDS row (80 bytes)
+constexpr float kF16Max = 65504.0f;
+
+// Two floats -> packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f16x2_t v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Saturate finite values to the fp16 range; NaN stays NaN.
+__device__ __forceinline__ float sat_f16(float v) { return fabsf(v) > kF16Max ? copysignf(kF16Max, v) : v; }
+
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// 16 consecutive weights of one row-block half -> 8 packed fp16 pairs.
+// BITS = 2: `code` holds 16 codes in one word (pair p at bits 2p / 16+2p).
+__device__ __forceinline__ void decode16_b2(uint32_t code, uint32_t smw, uint32_t (&out)[8]) {
+  const float s = f16lo(smw), m = f16hi(smw);
+  const uint32_t lut_lo = pack_f16(__builtin_fmaf(s, 0.f, m), __builtin_fmaf(s, 1.f, m));
+  const uint32_t lut_hi = pack_f16(__builtin_fmaf(s, 2.f, m), __builtin_fmaf(s, 3.f, m));
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t q2 = (code >> (2 * p)) & 0x00030003u;
+    const uint32_t sel = q2 * 0x0202u + 0x01000100u;  // bytes (2q, 2q+1) for each halfword
+    out[p] = __builtin_amdgcn_perm(lut_hi, lut_lo, sel);
+  }
+}
+
+// BITS = 4: two words, 8 codes each (pair p at bits 4p / 16+4p).
+__device__ __forceinline__ void decode16_b4(uint32_t c0, uint32_t c1, uint32_t smw, uint32_t (&out)[8]) {
+  const float s = f16lo(smw), m = f16hi(smw);
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t c = w ? c1 : c0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t q2 = (c >> (4 * p)) & 0x000F000Fu;
+      const float qe = (float)(q2 & 0xFFu), qo = (float)(q2 >> 16);
+      out[4 * w + p] = pack_f16(__builtin_fmaf(s, qe, m), __builtin_fmaf(s, qo, m));
+    }
+  }
+}
+
+struct TileInfo {
+  int32_t slot, m0;
+};
+
+// Build the M-tile list: for each active slot, ceil(n_e / BM) tiles.
+__global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ active,
+                                                          const int32_t* __restrict__ n_active, int BM,
+                                                          TileInfo* __restrict__ tiles, int32_t* __restrict__ count) {
+  __shared__ int sh[1024 / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int na = *n_active;
+  int running = 0;
+  for (int base = 0; base < na; base += 1024) {
+    const int s = base + tid;
+    int mt = 0, ne = 0;
+    if (s < na) {
+      const int e = active[s];
+      ne = offsets[e + 1] - offsets[e];
+      mt = (ne + BM - 1) / BM;
+    }
+    int inc = mt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += v;
+    }
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < 1024 / 64; ++w) {
+      if (w < wave) before += sh[w];
+      total += sh[w];
+    }
+    const int start = running + before + inc - mt;
+    for (int j = 0; j < mt; ++j) tiles[start + j] = TileInfo{s, j * BM};
+    running += total;
+    __syncthreads();
+  }
+  if (tid == 0) *count = running;
+}
+
+// x [n] (bf16 bits or fp32) -> fp16 (round to nearest even, saturating), 8 per thread.
+template <bool XF32>
+__global__ __launch_bounds__(256) void to_f16_kernel(const void* __restrict__ x, int64_t n8, uint4* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    float f[8];
+    if constexpr (XF32) {
+      const float4 a = reinterpret_cast<const float4*>(x)[2 * i], b = reinterpret_cast<const float4*>(x)[2 * i + 1];
+      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+      const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(w[j] << 16);
+        f[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    out[i] = make_uint4(pack_f16(sat_f16(f[0]), sat_f16(f[1])), pack_f16(sat_f16(f[2]), sat_f16(f[3])),
+                        pack_f16(sat_f16(f[4]), sat_f16(f[5])), pack_f16(sat_f16(f[6]), sat_f16(f[7])));
+  }
+}
+
+struct GemmArgs {
+  const uint8_t* base;
+  int64_t stride;
+  const int32_t* slot_map;
+  int H, I, k;
+  int64_t off_c0, off_s0, off_c1, off_s1;  // gate/up: Wg and Wu planes; down: Wd planes in c0/s0
+  const _Float16* a_src;                   // x [T x H] (gate/up) or h [n x I] (down), fp16
+  const int32_t* offsets;
+  const int32_t* sorted_assign;
+  const int32_t* active;
+  const TileInfo* tiles;
+  const int32_t* tile_count;
+  int n_tiles_n;
+  void* out;  // h [n x I] fp16 (gate/up) or y [T*k x H] (down)
+};
+
+template <int BITS, int BM, bool GATEUP, bool YBF16>
+__global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
+  constexpr int FM = BM / 32;  // 16-row fragments per wave
+  constexpr int A_CHUNKS = BM * 4 / 256;  // 16-byte chunks of the A tile per thread per K-step
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_b[2][kBN * kPitch];
+
+  const int tile_idx = blockIdx.x / A.n_tiles_n, nt = blockIdx.x % A.n_tiles_n;
+  if (tile_idx >= *A.tile_count) return;
+  const TileInfo ti = A.tiles[tile_idx];
+  const int e = A.active[ti.slot];
+  const int p_begin = A.offsets[e] + ti.m0;
+  const int rows = min(BM, A.offsets[e + 1] - p_begin);
+  const int idx = A.slot_map ? A.slot_map[e] : e;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = GATEUP ? A.H : A.I;
+  const int KS = K / kBK;
+
+  if (idx < 0) {  // expert not resident: NaN outputs, no weight reads
+    const float nan = __builtin_nanf("");
+    for (int c = tid; c < BM * kBN; c += 256) {
+      const int m = c / kBN, col = c % kBN;
+      if (m >= rows) continue;
+      if constexpr (GATEUP) {
+        const int g = col / 16, j = col % 16;
+        const int i = nt * 64 + 8 * g + j;
+        if (j < 8 && i < A.I)
+          reinterpret_cast<_Float16*>(A.out)[(size_t)(p_begin + m) * A.I + i] = (_Float16)nan;
+      } else {
+        const int n = nt * kBN + col;
+        const int64_t a = A.sorted_assign[p_begin + m];
+        if (n < A.H) {
+          if constexpr (YBF16) reinterpret_cast<__bf16*>(A.out)[a * A.H + n] = (__bf16)nan;
+          else reinterpret_cast<float*>(A.out)[a * A.H + n] = nan;
+        }
+      }
+    }
+    return;
+  }
+  const uint8_t* blob = A.base + (int64_t)idx * A.stride;
+
+  // ---- A-tile sources: row pointer per chunk this thread copies --------------
+  const uint8_t* a_row[A_CHUNKS];
+  int a_col16[A_CHUNKS];
+  bool a_ok[A_CHUNKS];
+#pragma unroll
+  for (int j = 0; j < A_CHUNKS; ++j) {
+    const int c = tid + 256 * j;
+    const int m = c / 4;
+    a_col16[j] = c % 4;
+    a_ok[j] = m < rows;
+    const int p = p_begin + (a_ok[j] ? m : 0);
+    if constexpr (GATEUP) {
+      const int64_t tok = A.sorted_assign[p] / A.k;
+      a_row[j] = reinterpret_cast<const uint8_t*>(A.a_src + tok * (int64_t)A.H);
+    } else {
+      a_row[j] = reinterpret_cast<const uint8_t*>(A.a_src + (int64_t)p * A.I);
+    }
+  }
+
+  // ---- B-tile source: this thread decodes 16 weights of one tile row ---------
+  const int b_r = tid >> 1, b_half = tid & 1;
+  bool b_ok;
+  const uint8_t* b_codes;
+  const uint8_t* b_sm;
+  {
+    int64_t row;
+    int64_t oc, os;
+    if constexpr (GATEUP) {
+      const int g = b_r / 16, j = b_r % 16;
+      const int i = nt * 64 + 8 * g + (j & 7);
+      b_ok = i < A.I;
+      row = b_ok ? i : 0;
+      oc = j < 8 ? A.off_c0 : A.off_c1;
+      os = j < 8 ? A.off_s0 : A.off_s1;
+    } else {
+      const int n = nt * kBN + b_r;
+      b_ok = n < A.H;
+      row = b_ok ? n : 0;
+      oc = A.off_c0;
+      os = A.off_s0;
+    }
+    b_codes = blob + oc + row * ((int64_t)K * BITS / 8);
+    b_sm = blob + os + row * ((int64_t)(K / 32) * 4);
+  }
+
+  uint4 a_reg[A_CHUNKS];
+  uint32_t b_code[BITS / 2 == 1 ? 1 : 2];
+  uint32_t b_smw;
+
+  auto load_stage = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < A_CHUNKS; ++j) {
+      a_reg[j] = a_ok[j] ? *reinterpret_cast<const uint4*>(a_row[j] + (int64_t)ks * kBK * 2 + a_col16[j] * 16)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    if (b_ok) {
+      if constexpr (BITS == 2) {
+        b_code[0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 8 + b_half * 4);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(b_codes + (int64_t)ks * 16 + b_half * 8);
+        b_code[0] = v.x;
+        b_code[1] = v.y;
+      }
+      b_smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
+    }
+  };
+
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < A_CHUNKS; ++j) {
+      const int c = tid + 256 * j;
+      const int m = c / 4;
+      *reinterpret_cast<uint4*>(&lds_a[buf][m * kPitch + a_col16[j] * 8]) = a_reg[j];
+    }
+    uint32_t w[8];
+    if (b_ok) {
+      if constexpr (BITS == 2) decode16_b2(b_code[0], b_smw, w);
+      else decode16_b4(b_code[0], b_code[1], b_smw, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = 0u;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(&lds_b[buf][b_r * kPitch + b_half * 16]);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  };
+
+  f32x4_t acc[FM][4];
+#pragma unroll
+  for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  const int frag_r = lane & 15, frag_k = (lane >> 4) * 8;
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) load_stage(ks + 1);
+    f16x8_t af[FM], bfr[4];
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi)
+      af[fi] = *reinterpret_cast<const f16x8_t*>(&lds_a[cur][(wm * (BM / 2) + 16 * fi + frag_r) * kPitch + frag_k]);
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj)
+      bfr[fj] = *reinterpret_cast<const f16x8_t*>(&lds_b[cur][(wn * 64 + 16 * fj + frag_r) * kPitch + frag_k]);
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj)
+        acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fi], bfr[fj], acc[fi][fj], 0, 0, 0);
+    if (ks + 1 < KS) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane = output column (lane & 15), rows 4*(lane >> 4) + r ----
+  const int col = lane & 15, rbase = 4 * (lane >> 4);
+#pragma unroll
+  for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[fi][fj][r];
+        const int m = wm * (BM / 2) + 16 * fi + rbase + r;
+        if constexpr (GATEUP) {
+          const float u = __shfl_xor(v, 8, 64);
+          const int i = nt * 64 + 8 * (4 * wn + fj) + col;
+          if (col < 8 && m < rows && i < A.I)
+            reinterpret_cast<_Float16*>(A.out)[(size_t)(p_begin + m) * A.I + i] =
+                (_Float16)sat_f16(v / (1.0f + expf(-v)) * u);
+        } else {
+          const int n = nt * kBN + wn * 64 + 16 * fj + col;
+          if (m < rows && n < A.H) {
+            const int64_t a = A.sorted_assign[p_begin + m];
+            if constexpr (YBF16) reinterpret_cast<__bf16*>(A.out)[a * A.H + n] = (__bf16)v;
+            else reinterpret_cast<float*>(A.out)[a * A.H + n] = v;
+          }
+        }
+      }
+}
+
+constexpr int kBM = 128;
+
+struct MfmaWs {
+  _Float16* x16;
+  _Float16* h;
+  TileInfo* tiles;
+  int32_t* count;
+  size_t bytes;
+};
+
+MfmaWs carve(uint8_t* ws, int T, int H, int n, int E, int I) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const int max_tiles = (int)ceil_div(n, kBM) + std::min(E, n);
+  MfmaWs w;
+  size_t off = 0;
+  w.x16 = reinterpret_cast<_Float16*>(ws + off);
+  off += up((size_t)T * H * 2);
+  w.h = reinterpret_cast<_Float16*>(ws + off);
+  off += up((size_t)n * I * 2);
+  w.tiles = reinterpret_cast<TileInfo*>(ws + off);
+  off += up((size_t)max_tiles * sizeof(TileInfo));
+  w.count = reinterpret_cast<int32_t*>(ws + off);
+  off += 256;
+  w.bytes = off;
+  return w;
+}
+
+template <int BITS, bool YBF16>
+moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, bool xf32, int T, int k,
+                      const int32_t* offsets, const int32_t* sorted_assign, const int32_t* active,
+                      const int32_t* n_active, void* y, uint8_t* ws, hipStream_t s) {
+  const int n = T * k;
+  const int max_active = (int)std::min<int64_t>(q.E, n);
+  const int max_tiles = (int)ceil_div(n, kBM) + max_active;
+  const MfmaWs W = carve(ws, T, q.H, n, q.E, q.I);
+
+  const int64_t n8 = (int64_t)T * q.H / 8;
+  const int cblocks = (int)std::min<int64_t>(4096, ceil_div(n8, 256));
+  if (xf32)
+    to_f16_kernel<true><<<cblocks, 256, 0, s>>>(x, n8, reinterpret_cast<uint4*>(W.x16));
+  else
+    to_f16_kernel<false><<<cblocks, 256, 0, s>>>(x, n8, reinterpret_cast<uint4*>(W.x16));
+  if (moe_status st = check_launch("mfma_to_f16")) return st;
+  mfma_tiles_kernel<<<1, 1024, 0, s>>>(offsets, active, n_active, kBM, W.tiles, W.count);
+  if (moe_status st = check_launch("mfma_tiles")) return st;
+
+  GemmArgs a;
+  a.base = reinterpret_cast<const uint8_t*>(q.base);
+  a.stride = q.stride;
+  a.slot_map = q.slot_map;
+  a.H = q.H;
+  a.I = q.I;
+  a.k = k;
+  a.offsets = offsets;
+  a.sorted_assign = sorted_assign;
+  a.active = active;
+  a.tiles = W.tiles;
+  a.tile_count = W.count;
+
+  // gate/up: N = 2I in tiles of 64 i values
+  a.off_c0 = L.gate_codes;
+  a.off_s0 = L.gate_sm;
+  a.off_c1 = L.up_codes;
+  a.off_s1 = L.up_sm;
+  a.a_src = W.x16;
+  a.n_tiles_n = (int)ceil_div(q.I, 64);
+  a.out = W.h;
+  launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, true, false>,
+           dim3((unsigned)(max_tiles * a.n_tiles_n)), dim3(256), 0, s, a);
+  if (moe_status st = check_launch("mfma_gateup")) return st;
+
+  // down: N = H in tiles of 128
+  a.off_c0 = L.down_codes;
+  a.off_s0 = L.down_sm;
+  a.a_src = W.h;
+  a.n_tiles_n = (int)ceil_div(q.H, kBN);
+  a.out = y;
+  launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, false, YBF16>,
+           dim3((unsigned)(max_tiles * a.n_tiles_n)), dim3(256), 0, s, a);
+  return check_launch("mfma_down");
+}
+
+}  // namespace
+
+size_t ffn_mfma_ws_bytes(int T, int k, int E, int H, int I) { return carve(nullptr, T, H, T * k, E, I).bytes; }
+
+moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
+                           const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
+                           moe_dtype y_t, void* ws, hipStream_t s) {
+  const BlobLayout L = blob_layout(q.H, q.I, q.bits);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  const bool xf = x_t == MOE_F32, yb = y_t == MOE_BF16;
+  if (q.bits == 2)
+    return yb ? launch_all<2, true>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s)
+              : launch_all<2, false>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s);
+  return yb ? launch_all<4, true>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s)
+            : launch_all<4, false>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s);
 }
 
 }  // namespace moe

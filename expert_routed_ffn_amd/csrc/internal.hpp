@@ -42,7 +42,7 @@ moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, in
                            const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
                            moe_dtype y_t, void* ws, hipStream_t s);
 
-size_t ffn_mfma_ws_bytes(int n_assign, int E, int I);
+size_t ffn_mfma_ws_bytes(int T, int k, int E, int H, int I);
 moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
                            const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
                            moe_dtype y_t, void* ws, hipStream_t s);

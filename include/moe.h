@@ -79,7 +79,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_ffn_path {
   MOE_PATH_AUTO = 0,
   MOE_PATH_GEMV = 1, /* fused dequant-GEMV, fp32 throughout: decode and verify steps */
-  MOE_PATH_MFMA = 2  /* weights dequantized to bf16 in LDS, bf16 MFMA, fp32 accumulate: prefill */
+  MOE_PATH_MFMA = 2  /* weights decoded to fp16 in LDS, fp16 MFMA, fp32 accumulate: prefill */
 } moe_ffn_path;
 
 /* One layer's experts.  Expert e's blob is at base + idx(e) * stride where
@@ -147,8 +147,8 @@ moe_status moe_dispatch(const int32_t* ids, int T, int k, int E, int32_t* offset
  *   y        [T x k x H] out, dtype y_t; rows of dropped assignments are untouched.
  *   path     MOE_PATH_GEMV keeps g, u, h and the sums in fp32 (the bf16 dot
  *            instructions see x exactly, and fp32 values as a sum of two bf16
- *            parts); MOE_PATH_MFMA rounds the decoded weights and h to bf16
- *            and accumulates in fp32.
+ *            parts); MOE_PATH_MFMA rounds the decoded weights, x and h to fp16
+ *            (saturating at +-65504) and accumulates in fp32.
  *   ws       device scratch of at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE.
  */
