@@ -8,15 +8,17 @@ bf16 activations N(0, 1), fp32 router logits N(0, 1) plus a Zipf(1.1)
 popularity bias.  All inputs are seeded synthetic data (no trained weights).
 
 A step is one pass of the whole layer: route + dispatch + expert FFN +
-combine.  Step i uses layer copy i mod --copies (independent allocations of
+combine, issued as moe_layer_decode (three launches: routing and dispatch in one
+workgroup, the gate/up GEMV, the down GEMV with the combine folded in); the
+same step as four separate calls is timed beside it.  Step i uses layer copy i mod --copies (independent allocations of
 the same layer, 48 by default, about 1 GB of touched weights per cycle) so
 that the 256 MB on-package cache cannot serve one step from the previous one;
 this is the 48-layer stack of the 125B-shaped model with identical weights.
 The K timed steps are captured once in a HIP graph and replayed.
 
 The JSON line also carries:
-  roofline      the dominant kernel (expert gate/up GEMV): algorithmic bytes
-                per launch / its mean duration, timed with HIP events attached
+  roofline      the dominant kernel (the gate/up dequant-GEMV): algorithmic
+                bytes per launch / its mean duration, timed with HIP events attached
                 to that kernel's own launch (moe_profile_next_launch);
   cpu_baseline  the CPU oracle (scalar C, fp64, one thread) on a bounded
                 sample of the same layer steps;
@@ -111,7 +113,12 @@ def decode_bench(args, torch, moe, synth, oracle):
         "out": torch.empty((T, w.H), dtype=torch.float32, device=dev),
     }
 
+    bufs["dws"] = torch.empty(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8, device=dev)
+
     def step(i, stream=None):
+        moe.layer_decode(layers[i % NL], x, lg, k, bufs=bufs, stream=stream)
+
+    def step4(i, stream=None):
         moe.layer_forward(layers[i % NL], x, lg, k, bufs=bufs, path="gemv", stream=stream)
 
     # correctness guard on the benchmarked buffers: copy NL-1 against the oracle
@@ -144,19 +151,39 @@ def decode_bench(args, torch, moe, synth, oracle):
     if not np.array_equal(got, got2):
         raise SystemExit("bench: graph replay output differs from the eager step")
 
-    # dominant kernel: gate/up GEMV, timed per launch with events attached to it
-    nprof = max(NL, 96)
+    # the same step as four separate calls, for comparison
+    k4 = max(NL, args.steps // 4)
+    g4 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g4, stream=cap):
+        for i in range(k4):
+            step4(i)
+    g4.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g4.replay()
+    torch.cuda.synchronize()
+    four_call_us = (time.perf_counter() - t0) / k4 * 1e6
+    if not np.array_equal(got, bufs["out"].cpu().numpy().astype(np.float64)):
+        raise SystemExit("bench: the four-call step differs from the fused step")
+
+    # dominant kernel: the gate/up GEMV (two thirds of the bytes); the down
+    # kernel (with the folded combine) is timed on alternate steps
+    nprof = 2 * max(NL, 96)
     timer = KernelTimer(nprof)
     for i in range(nprof):
-        timer.arm(i, "gemv_gateup")
-        moe.expert_ffn_q(layers[i % NL], x, k, bufs["dispatch"], bufs["y"], path="gemv", ws=bufs["ws"])
+        timer.arm(i, "gemv_gateup" if i % 2 == 0 else "gemv_down")
+        step(i // 2)
     torch.cuda.synchronize()
     kt = timer.times_ms()
     timer.close()
-    # the first cycle pays first-touch costs; use the rest
-    kt = kt[NL:] if len(kt) > NL else kt
-    gu_ms = sum(kt) / len(kt)
-    gu_bytes = U * 2 * (w.I * w.H * w.bits // 8 + w.I * (w.H // 32) * 4) + T * w.H * 2 + T * k * w.I * 4
+    # the first cycle of copies pays first-touch costs; use the rest
+    gu = kt[0::2][NL:] if len(kt) // 2 > NL else kt[0::2]
+    dn = kt[1::2][NL:] if len(kt) // 2 > NL else kt[1::2]
+    gu_ms = sum(gu) / len(gu)
+    dn_ms = sum(dn) / len(dn)
+    gu_plane = w.I * w.H * w.bits // 8 + w.I * (w.H // 32) * 4  # one [I x H] matrix: codes + scale/min
+    gu_bytes = U * 2 * gu_plane + T * w.H * 2 + T * k * w.I * 4  # Wg, Wu of the unique experts; x; h written
+    dn_bytes = U * (eb - 2 * gu_plane) + T * k * w.I * 4 + T * k * w.H * 4 + T * w.H * 4  # Wd; h; y; out
 
     res = {
         "value": T * args.steps / elapsed,
@@ -174,10 +201,13 @@ def decode_bench(args, torch, moe, synth, oracle):
             "kernel": "ffn_gateup_kernel (expert gate/up dequant-GEMV + SwiGLU)",
             "bytes_per_launch": gu_bytes,
             "mean_us": gu_ms * 1e3,
-            "launches": len(kt),
+            "launches": len(gu),
+            "down_kernel_mean_us": dn_ms * 1e3,
+            "down_kernel_gbs": dn_bytes / (dn_ms * 1e-3) / 1e9,
         },
         "layer_hbm_frac": (U * eb + T * w.H * 2 + T * w.E * 4 + T * w.H * 4) / (elapsed / args.steps) / 1e9
         / HBM_PEAK_GBS,
+        "four_call_us_per_step": four_call_us,
     }
     return res, (x_np, lg_np, ex, w)
 
@@ -326,7 +356,8 @@ def main():
                         "2-bit block-32 weights (fp16 scale/min), bf16 activations, Zipf(1.1) router bias",
             "E": 512, "k": 10, "H": 2048, "I": 512, "T": 3, "bits": 2,
             "layer_copies": args.copies, "hip_graph": True, "unique_experts_per_step": res["U"],
-            "layer_hbm_frac": res["layer_hbm_frac"],
+            "layer_hbm_frac": res["layer_hbm_frac"], "entry": "moe_layer_decode",
+            "four_call_us_per_step": res["four_call_us_per_step"],
         },
         "roofline": res["roofline"],
         "cpu_baseline": cpu,

@@ -138,7 +138,7 @@ static moe_ffn_path resolve_path(moe_ffn_path p, int T) {
 size_t moe_expert_ffn_workspace_bytes(const moe_qlayer* q, int T, int k, moe_ffn_path path) {
   if (!q || T < 0 || k < 1) return 0;
   const int n = T * k;
-  if (resolve_path(path, T) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(n, q->I);
+  if (resolve_path(path, T) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(T, k, q->E, q->H, q->I);
   return ffn_mfma_ws_bytes(T, k, q->E, q->H, q->I);
 }
 
@@ -162,7 +162,8 @@ moe_status moe_expert_ffn_q(const moe_qlayer* q, const void* x, moe_dtype x_t, i
   if (q->stride < eb || q->stride % 256)
     return fail(MOE_EINVAL, fmt("moe_expert_ffn_q: stride %lld (needs >= %lld and a multiple of 256)", q->stride, eb));
   if (!aligned(q->base, 256)) return fail(MOE_EINVAL, "moe_expert_ffn_q: base not 256-byte aligned");
-  if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_EINVAL, "moe_expert_ffn_q: x or y not 16-byte aligned");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256))
+    return fail(MOE_EINVAL, "moe_expert_ffn_q: x or y not 16-byte aligned, or ws not 256-byte aligned");
   const moe_ffn_path p = resolve_path(path, T);
   const size_t need = moe_expert_ffn_workspace_bytes(q, T, k, p);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -171,6 +172,50 @@ moe_status moe_expert_ffn_q(const moe_qlayer* q, const void* x, moe_dtype x_t, i
   if (p == MOE_PATH_GEMV)
     return launch_ffn_gemv(*q, x, x_t, T, k, offsets, sorted_assign, active, n_active, y, y_t, ws, stream);
   return launch_ffn_mfma(*q, x, x_t, T, k, offsets, sorted_assign, active, n_active, y, y_t, ws, stream);
+}
+
+size_t moe_layer_decode_workspace_bytes(const moe_qlayer* q, int T, int k) {
+  if (!q || T < 0 || k < 1 || q->E < 1) return 0;
+  return decode_ws(nullptr, T, k, q->E, q->H, q->I).bytes;
+}
+
+moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void* x, moe_dtype x_t, int T, int k,
+                            const void* residual, moe_dtype r_t, int32_t* ids, float* w, int32_t* offsets,
+                            int32_t* sorted_assign, int32_t* assign_pos, int32_t* active, int32_t* n_active, void* y,
+                            moe_dtype y_t, float* out, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  const char* fn = "moe_layer_decode";
+  if (!q) return fail(MOE_EINVAL, "moe_layer_decode: null moe_qlayer");
+  if (T < 0) return fail(MOE_EINVAL, "moe_layer_decode: T < 0");
+  if (T > kDescT) return fail(MOE_EUNSUPPORTED, fmt("moe_layer_decode: T=%lld above 12", T));
+  if (moe_status st = check_ek(fn, q->E, k)) return st;
+  if (moe_status st = check_shape(fn, q->H, q->I, q->bits)) return st;
+  if (x_t != MOE_F32 && x_t != MOE_BF16) return fail(MOE_EINVAL, "moe_layer_decode: x dtype");
+  if (y_t != MOE_F32 && y_t != MOE_BF16) return fail(MOE_EINVAL, "moe_layer_decode: y dtype");
+  if (residual && r_t != MOE_F32 && r_t != MOE_BF16) return fail(MOE_EINVAL, "moe_layer_decode: residual dtype");
+  if (T == 0) return MOE_OK;
+  if (!q->base || !logits || !x || !ids || !w || !offsets || !sorted_assign || !assign_pos || !active || !n_active ||
+      !y || !out)
+    return fail(MOE_EINVAL, "moe_layer_decode: null pointer");
+  const int64_t eb = blob_layout(q->H, q->I, q->bits).bytes;
+  if (q->stride < eb || q->stride % 256)
+    return fail(MOE_EINVAL, fmt("moe_layer_decode: stride %lld (needs >= %lld and a multiple of 256)", q->stride, eb));
+  if (!aligned(q->base, 256)) return fail(MOE_EINVAL, "moe_layer_decode: base not 256-byte aligned");
+  const uintptr_t r_align = r_t == MOE_F32 ? 16 : 8;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
+      (residual && !aligned(residual, r_align)) || (out_bf16 && !aligned(out_bf16, 8)))
+    return fail(MOE_EINVAL, "moe_layer_decode: misaligned buffer");
+  const DecodeWs W = decode_ws(ws, T, k, q->E, q->H, q->I);
+  if (ws_bytes < W.bytes)
+    return fail(MOE_EWORKSPACE, fmt("moe_layer_decode: workspace %lld bytes, needs %lld", (long long)ws_bytes,
+                                    (long long)W.bytes));
+  if (moe_status st = launch_route_dispatch_decode(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
+                                                   active, n_active, W, stream))
+    return st;
+  if (moe_status st = launch_ffn_gemv_fused(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, w, residual, r_t,
+                                            out, out_bf16, false, stream))
+    return st;
+  return launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
 }
 
 moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,
@@ -190,7 +235,7 @@ moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int 
 }
 
 moe_status moe_profile_next_launch(moe_kernel kernel, hipEvent_t start, hipEvent_t stop) {
-  if ((int)kernel < 0 || (int)kernel > (int)MOE_KERNEL_COMBINE) return fail(MOE_EINVAL, "moe_profile_next_launch: kernel");
+  if ((int)kernel < 0 || (int)kernel > (int)MOE_KERNEL_DECODE_PREP) return fail(MOE_EINVAL, "moe_profile_next_launch: kernel");
   if (!start || !stop) return fail(MOE_EINVAL, "moe_profile_next_launch: null event");
   ProfileReq& p = profile_req();
   p.kernel = (int)kernel;

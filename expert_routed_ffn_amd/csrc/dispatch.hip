@@ -17,70 +17,16 @@
 // Larger n: (A) per 1024-assignment chunk, ranks within the chunk and the
 // chunk's per-expert counts; (B) one workgroup turns counts into per-chunk
 // bases and offsets; (C) scatter.
-#include "internal.hpp"
+#include "route_dispatch_dev.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBlock = 1024;
-constexpr int kWaves = kBlock / 64;
+using dev::kDispBlock;
+using dev::kDispWaves;
+using dev::kSentinel;
+constexpr int kBlock = kDispBlock;
 constexpr int kSmallN = 4096;
-constexpr int kSentinel = 2047;  // 11 bits; never a valid id (E <= 1024)
-
-__device__ __forceinline__ uint64_t match_peers(int key) {
-  uint64_t peers = ~0ull;
-#pragma unroll
-  for (int b = 0; b < 11; ++b) {
-    const bool bit = (key >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  return peers;
-}
-
-// Exclusive scan over the block of two values at once; returns the totals.
-__device__ __forceinline__ void block_exclusive_scan2(int v0, int v1, int& ex0, int& ex1, int& tot0, int& tot1,
-                                                      int* sh /* [2 * kWaves] */) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int s0 = v0, s1 = v1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int a0 = __shfl_up(s0, off, 64), a1 = __shfl_up(s1, off, 64);
-    if (lane >= off) { s0 += a0; s1 += a1; }
-  }
-  if (lane == 63) { sh[wave] = s0; sh[kWaves + wave] = s1; }
-  __syncthreads();
-  int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    const int c0 = sh[w], c1 = sh[kWaves + w];
-    if (w < wave) { b0 += c0; b1 += c1; }
-    t0 += c0;
-    t1 += c1;
-  }
-  ex0 = b0 + s0 - v0;
-  ex1 = b1 + s1 - v1;
-  tot0 = t0;
-  tot1 = t1;
-  __syncthreads();
-}
-
-// Counts -> offsets, cursor (LDS copy of offsets), active list, n_active.
-__device__ __forceinline__ void offsets_and_active(const int* cnt_lds, int E, int32_t* offsets, int* cursor,
-                                                   int32_t* active, int32_t* n_active, int* scan_sh) {
-  const int tid = threadIdx.x;
-  const int c = tid < E ? cnt_lds[tid] : 0;
-  int exc, exf, totc, totf;
-  block_exclusive_scan2(c, c > 0 ? 1 : 0, exc, exf, totc, totf, scan_sh);
-  if (tid < E) {
-    offsets[tid] = exc;
-    if (cursor) cursor[tid] = exc;
-    if (c > 0) active[exf] = tid;
-  }
-  if (tid == 0) {
-    offsets[E] = totc;
-    *n_active = totf;
-  }
-}
 
 __global__ __launch_bounds__(kBlock) void dispatch_small_kernel(const int32_t* __restrict__ ids, int n, int E,
                                                                 int32_t* __restrict__ offsets,
@@ -88,40 +34,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_small_kernel(const int32_t* _
                                                                 int32_t* __restrict__ assign_pos,
                                                                 int32_t* __restrict__ active,
                                                                 int32_t* __restrict__ n_active) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int cursor[kMaxE];
-  __shared__ int scan_sh[2 * kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < E) cnt[tid] = 0;
-  __syncthreads();
-  for (int a = tid; a < n; a += kBlock) {
-    const int e = ids[a];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  offsets_and_active(cnt, E, offsets, cursor, active, n_active, scan_sh);
-  __syncthreads();
-
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int base = 0; base < n; base += kBlock) {
-    const int a = base + tid;
-    const bool valid = a < n;
-    const int e = valid ? ids[a] : -1;
-    const bool ok = valid && (unsigned)e < (unsigned)E;
-    const uint64_t peers = match_peers(ok ? e : kSentinel);
-    const int rank = __popcll(peers & lt), cnt_w = __popcll(peers);
-    const int nw = (int)min((int64_t)kWaves, ceil_div(n - base, 64));
-    for (int w = 0; w < nw; ++w) {
-      if (wave == w && ok) {
-        const int pos = cursor[e] + rank;
-        sorted_assign[pos] = a;
-        assign_pos[a] = pos;
-        if (rank == cnt_w - 1) cursor[e] = pos + 1;
-      }
-      __syncthreads();
-    }
-    if (valid && !ok) assign_pos[a] = -1;
-  }
+  __shared__ dev::DispatchLds L;
+  dev::dispatch_block(ids, n, E, offsets, sorted_assign, assign_pos, active, n_active, L);
 }
 
 // (A) ranks inside each 1024-assignment chunk and the chunk's counts per expert.
@@ -137,10 +51,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_rank_kernel(const int32_t* __
   const bool valid = a < n;
   const int e = valid ? ids[a] : -1;
   const bool ok = valid && (unsigned)e < (unsigned)E;
-  const uint64_t peers = match_peers(ok ? e : kSentinel);
+  const uint64_t peers = dev::match_peers(ok ? e : kSentinel);
   const uint64_t lt = (1ull << lane) - 1ull;
   const int rank = __popcll(peers & lt), cnt_w = __popcll(peers);
-  const int nw = (int)min((int64_t)kWaves, ceil_div(n - base, 64));
+  const int nw = (int)min((int64_t)kDispWaves, ceil_div(n - base, 64));
   for (int w = 0; w < nw; ++w) {
     if (wave == w && ok) {
       const int r = cursor[e] + rank;
@@ -158,7 +72,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_scan_kernel(int nchunks, int 
                                                                int32_t* __restrict__ active,
                                                                int32_t* __restrict__ n_active) {
   __shared__ int cnt[kMaxE];
-  __shared__ int scan_sh[2 * kWaves];
+  __shared__ int scan_sh[2 * kDispWaves];
   const int tid = threadIdx.x;
   if (tid < E) {
     int run = 0;
@@ -170,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_scan_kernel(int nchunks, int 
     cnt[tid] = run;
   }
   __syncthreads();
-  offsets_and_active(cnt, E, offsets, nullptr, active, n_active, scan_sh);
+  dev::offsets_and_active(cnt, E, offsets, nullptr, active, n_active, scan_sh);
 }
 
 // (C) scatter to the sorted positions.
@@ -192,6 +106,57 @@ __global__ __launch_bounds__(kBlock) void dispatch_scatter_kernel(const int32_t*
   assign_pos[a] = pos;
 }
 
+// Decode step, part 1: route all T tokens (one wave per token, the same
+// routine as the stand-alone routing kernel), dispatch in LDS (the same
+// routine as dispatch_small_kernel), then write the per-expert descriptors the
+// persistent FFN kernel reads and clear its counters.
+template <int EPL>
+__global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc,
+    int32_t* __restrict__ done, int32_t* __restrict__ cnt, int n_cnt, int32_t* __restrict__ flag) {
+  __shared__ dev::DispatchLds L;
+  __shared__ int32_t ids_lds[kBlock];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = wave; t < T; t += kDispWaves) {
+    int id;
+    float wt;
+    dev::route_token<EPL>(logits + (size_t)t * E, E, k, id, wt);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = wt;
+      ids_lds[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  const int n = T * k;
+  dev::dispatch_block(ids_lds, n, E, offsets, sorted_assign, assign_pos, active, n_active, L);
+  __syncthreads();
+  // descriptors: the dispatch results are in global memory written by this block
+  __threadfence_block();
+  const int na = *n_active;
+  const int max_active = min(E, n);
+  for (int s2 = tid; s2 < max_active; s2 += kBlock) {
+    done[s2] = 0;
+    if (s2 >= na) continue;
+    SlotDesc d;
+    d.e = active[s2];
+    d.p0 = offsets[d.e];
+    d.ne = offsets[d.e + 1] - d.p0;
+    d.pad = 0;
+    for (int j = 0; j < kDescT; ++j) {
+      const int a = j < d.ne ? sorted_assign[d.p0 + j] : 0;
+      d.asg[j] = a;
+      d.tok[j] = a / k;
+    }
+    for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
+    desc[s2] = d;
+  }
+  for (int i = tid; i < n_cnt; i += kBlock) cnt[i] = 0;
+  if (tid == 0) *flag = 0;
+}
+
 __global__ void dispatch_empty_kernel(int E, int32_t* offsets, int32_t* n_active) {
   for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = 0;
   if (threadIdx.x == 0) *n_active = 0;
@@ -203,6 +168,20 @@ size_t dispatch_ws_bytes(int n, int E) {
   if (n <= kSmallN) return 0;
   const int64_t nchunks = ceil_div(n, kBlock);
   return (size_t)(((int64_t)n + nchunks * E) * 4 + 256);
+}
+
+moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                        int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                                        int32_t* active, int32_t* n_active, const DecodeWs& W, hipStream_t s) {
+  const int epl = (int)ceil_div(E, 64);
+  const auto kern = epl <= 1   ? route_dispatch_decode_kernel<1>
+                    : epl <= 2 ? route_dispatch_decode_kernel<2>
+                    : epl <= 4 ? route_dispatch_decode_kernel<4>
+                    : epl <= 8 ? route_dispatch_decode_kernel<8>
+                               : route_dispatch_decode_kernel<16>;
+  launch_k(MOE_KERNEL_ROUTE, kern, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, ids, w, offsets, sorted_assign,
+           assign_pos, active, n_active, W.desc, W.done, W.cnt, W.n_cnt, W.flag);
+  return check_launch("route_dispatch_decode");
 }
 
 moe_status launch_dispatch(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* sorted_assign,

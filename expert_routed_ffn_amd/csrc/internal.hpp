@@ -37,10 +37,45 @@ size_t dispatch_ws_bytes(int n, int E);
 moe_status launch_dispatch(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* sorted_assign,
                            int32_t* assign_pos, int32_t* active, int32_t* n_active, void* ws, hipStream_t s);
 
-size_t ffn_gemv_ws_bytes(int n_assign, int I);
+// ---- decode path (GEMV) ---------------------------------------------------
+// Per active expert: its id, first sorted position, row count and (for the
+// first kDescT rows) each row's token and assignment index.  128 bytes.
+constexpr int kDescT = 12;
+struct SlotDesc {
+  int32_t e, p0, ne, pad;
+  int32_t tok[kDescT];
+  int32_t asg[kDescT];
+  int32_t pad2[4];
+};
+static_assert(sizeof(SlotDesc) == 128, "SlotDesc is one 128-byte record");
+
+// Decode workspace: h [T*k x I] fp32, slot descriptors, per-slot gate/up
+// completion counters, per-(token, column tile) combine counters, a flag.
+struct DecodeWs {
+  float* h;
+  SlotDesc* desc;
+  int32_t* done;
+  int32_t* cnt;
+  int32_t* flag;
+  int n_cnt;
+  size_t bytes;
+};
+DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I);
+
+size_t ffn_gemv_ws_bytes(int T, int k, int E, int H, int I);
 moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
                            const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
                            moe_dtype y_t, void* ws, hipStream_t s);
+
+// Fused decode step: route + dispatch + descriptors in one workgroup, then the
+// persistent FFN kernel with the combine folded in.
+moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                        int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                                        int32_t* active, int32_t* n_active, const DecodeWs& W, hipStream_t s);
+moe_status launch_ffn_gemv_fused(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
+                                 const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
+                                 moe_dtype y_t, const float* w, const void* residual, moe_dtype r_t, float* out,
+                                 uint16_t* out_bf16, bool combine, hipStream_t s);
 
 size_t ffn_mfma_ws_bytes(int T, int k, int E, int H, int I);
 moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,

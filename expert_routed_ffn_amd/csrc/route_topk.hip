@@ -6,45 +6,18 @@
 // the lower expert id first, -0.0 equals +0.0.  Weights: softmax over the k
 // selected logits.
 //
-// One wave64 per token.  Each lane owns E/64 logits (lane-strided, so the row
-// is read with coalesced loads).  A logit becomes a 64-bit key whose order is
-// the ranking order: the high word maps the float to an unsigned integer that
-// sorts like the float (sign-magnitude to offset binary; +0 and -0 share one
-// key), the low word is ~id so that a lower id wins a tie.  Keys are unique,
-// so k rounds of "lane max, then wave max, owner drops it" give the top k
-// exactly, with no floating-point comparisons.
-#include "internal.hpp"
+// One wave64 per token (the per-token routine is shared with the fused decode
+// step).  Each lane owns E/64 logits (lane-strided, so the row is read with
+// coalesced loads).  A logit becomes a 64-bit key whose order is the ranking
+// order: the high word maps the float to an unsigned integer that sorts like
+// the float (sign-magnitude to offset binary; +0 and -0 share one key), the
+// low word is ~id so that a lower id wins a tie.  Keys are unique, so k rounds
+// of "lane max, then wave max, owner drops it" give the top k exactly, with no
+// floating-point comparisons.
+#include "route_dispatch_dev.hpp"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ uint64_t rank_key(float f, int e) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) == 0) u = 0;  // -0.0 -> +0.0
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
-}
-
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
-  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-  return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
 template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
@@ -52,34 +25,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-
-  uint64_t key[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = (e < E) ? rank_key(row[e], e) : 0ull;  // 0 is below every real key
-  }
-
-  uint64_t mine = 0;  // lane j < k ends up holding the j-th selected key
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int j = 1; j < EPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (key[j] == best) key[j] = 0;
-    if (lane == r) mine = best;
-  }
-
-  const float lj = key_logit(mine);
-  const float l0 = __shfl(lj, 0, 64);
-  const float ex = (lane < k) ? expf(lj - l0) : 0.0f;
-  const float den = wave_sum_f32(ex);
+  int id;
+  float wt;
+  dev::route_token<EPL>(logits + (size_t)t * E, E, k, id, wt);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = (int32_t)(~(uint32_t)mine);
-    w[(size_t)t * k + lane] = ex / den;
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 

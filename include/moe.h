@@ -171,6 +171,25 @@ moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int 
                        moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t stream);
 
 /*
+ * moe_layer_decode -- the whole layer for decode and verify steps (T <= 12)
+ * in four launches: routing + dispatch + expert descriptors in one
+ * workgroup, the gate/up + SwiGLU kernel, the down kernel, the combine.  Passage: as for the four
+ * calls above (Strata feature, summary row "핵심 기법" and section
+ * "2. 왜 대단한가" (1)-(3)).  Every output (ids, w, the dispatch arrays, y,
+ * out, out_bf16) is bit-identical to moe_route_topk + moe_dispatch +
+ * moe_expert_ffn_q(MOE_PATH_GEMV) + moe_combine on the same inputs.
+ *   logits [T x E] fp32; x [T x H] (MOE_F32 or MOE_BF16); residual NULL or [T x H].
+ *   Outputs as in the four calls; ws of moe_layer_decode_workspace_bytes bytes.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (T > 12 or the limits above), MOE_EWORKSPACE.
+ */
+size_t moe_layer_decode_workspace_bytes(const moe_qlayer* q, int T, int k);
+moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void* x, moe_dtype x_t, int T, int k,
+                            const void* residual, moe_dtype r_t, int32_t* ids, float* w, int32_t* offsets,
+                            int32_t* sorted_assign, int32_t* assign_pos, int32_t* active, int32_t* n_active, void* y,
+                            moe_dtype y_t, float* out, uint16_t* out_bf16, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
  * Resident-expert slot table.
  * Passage: the most-called experts stay resident in GPU memory while all of
  * them sit in host RAM; a routed expert that is resident is used at once and
@@ -234,8 +253,9 @@ void moe_slot_table_destroy(moe_slot_table* t);
 typedef enum moe_kernel {
   MOE_KERNEL_ROUTE = 0,
   MOE_KERNEL_DISPATCH = 1,
-  MOE_KERNEL_GEMV_GATEUP = 2,
-  MOE_KERNEL_GEMV_DOWN = 3,
+  MOE_KERNEL_GEMV_GATEUP = 2, /* decode gate/up + SwiGLU */
+  MOE_KERNEL_GEMV_DOWN = 3,   /* decode down (+ the folded combine of moe_layer_decode) */
+  MOE_KERNEL_DECODE_PREP = 7, /* descriptor preparation of the stand-alone GEMV path */
   MOE_KERNEL_MFMA_GATEUP = 4,
   MOE_KERNEL_MFMA_DOWN = 5,
   MOE_KERNEL_COMBINE = 6

@@ -95,3 +95,16 @@ def test_combine_argument_checks():
     assert _st(L.moe_combine(fake, 0, fake, 2, 17, 64, NULL, 0, fake, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
     assert _st(L.moe_combine(fake, 0, fake, 2, 2, 66, NULL, 0, fake, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
     assert _st(L.moe_combine(fake, 5, fake, 2, 2, 64, NULL, 0, fake, NULL, NULL)) == _lib.MOE_EINVAL
+
+
+def test_layer_decode_argument_checks():
+    fake = ctypes.c_void_p(0x1000)
+    q = _q()
+    def call(T=3, k=2, ws_bytes=1 << 20):
+        return _st(L.moe_layer_decode(ctypes.byref(q), fake, fake, 1, T, k, None, 0, fake, fake, fake, fake, fake,
+                                      fake, fake, fake, 0, fake, None, ctypes.c_void_p(0x100000), ws_bytes, None))
+    assert call(T=13) == _lib.MOE_EUNSUPPORTED
+    assert call(k=17) == _lib.MOE_EUNSUPPORTED
+    assert call(T=0) == _lib.MOE_OK
+    assert call(ws_bytes=0) == _lib.MOE_EWORKSPACE
+    assert int(L.moe_layer_decode_workspace_bytes(ctypes.byref(q), 3, 2)) > 0

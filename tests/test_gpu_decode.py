@@ -229,3 +229,110 @@ def test_not_resident_expert_gives_nan_rows(moe):
     ids, wt, d, y, out = moe.layer_forward(layer, to_dev_x(w.x()), to_dev(lg), w.k)
     yy = to_host(y)
     assert np.all(np.isnan(yy[1, 0])) and np.all(np.isfinite(yy[0])) and np.all(np.isfinite(yy[1, 1]))
+
+
+# ---- fused decode step: moe_layer_decode --------------------------------------------
+
+def _four_calls_and_fused(moe, w, x, lg, ex, residual=None, y_dtype=None, out_bf16=False):
+    import torch
+    y_dtype = y_dtype or torch.float32
+    base = to_dev(ex)
+    layer = moe.ExpertLayer(w.E, w.H, w.I, w.bits, base)
+    xd, ld = to_dev_x(x), to_dev(lg)
+    res = None if residual is None else residual
+    ob4 = torch.zeros((w.T, w.H), dtype=torch.int16, device="cuda") if out_bf16 else None
+    obf = torch.zeros((w.T, w.H), dtype=torch.int16, device="cuda") if out_bf16 else None
+    a = moe.layer_forward(layer, xd, ld, w.k, residual=res, path="gemv", y_dtype=y_dtype, out_bf16=ob4)
+    b = moe.layer_decode(layer, xd, ld, w.k, residual=res, y_dtype=y_dtype, out_bf16=obf)
+    torch.cuda.synchronize()
+    return a, b, ob4, obf
+
+
+def _assert_bit_identical(a, b, n):
+    ids_a, w_a, d_a, y_a, o_a = a
+    ids_b, w_b, d_b, y_b, o_b = b
+    assert np.array_equal(to_host(ids_a), to_host(ids_b))
+    assert np.array_equal(to_host(w_a).view(np.uint32), to_host(w_b).view(np.uint32))
+    for f in ("offsets", "sorted_assign", "assign_pos", "active", "n_active"):
+        ta, tb = to_host(getattr(d_a, f)), to_host(getattr(d_b, f))
+        if f in ("sorted_assign", "assign_pos"):
+            ta, tb = ta[:n], tb[:n]
+        if f == "active":
+            na = int(to_host(d_a.n_active)[0])
+            ta, tb = ta[:na], tb[:na]
+        assert np.array_equal(ta, tb), f
+    ya, yb = to_host(y_a), to_host(y_b)
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    assert np.array_equal(to_host(o_a).view(np.uint32), to_host(o_b).view(np.uint32))
+
+
+@pytest.mark.parametrize("case", ["tiny", "decode_verify", "sweep1", "sweep2", "sweep4", "sweep8"])
+def test_layer_decode_bit_identical_to_four_calls(moe, case):
+    if case == "tiny":
+        w = synth.tiny()
+        lg = w.logits()
+        ex = w.experts()
+    else:
+        w = synth.decode_verify() if case == "decode_verify" else synth.decode_sweep(int(case[5:]))
+        lg = w.logits()
+        ex = routed_experts(w, lg)
+    x = w.x()
+    a, b, _, _ = _four_calls_and_fused(moe, w, x, lg, ex)
+    _assert_bit_identical(a, b, w.T * w.k)
+    ref = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits)
+    assert row_rel_err(to_host(b[4]), ref["out"]) <= DECODE_TOL
+
+
+@pytest.mark.parametrize("r_dtype,y_bf16", [("f32", False), ("bf16", True)])
+def test_layer_decode_residual_bf16_outputs(moe, r_dtype, y_bf16):
+    import torch
+    w = synth.decode_verify()
+    lg = w.logits()
+    ex = routed_experts(w, lg)
+    x = w.x()
+    xr = to_dev_x(x)
+    res = xr if r_dtype == "bf16" else xr.float()
+    a, b, ob4, obf = _four_calls_and_fused(moe, w, x, lg, ex, residual=res,
+                                           y_dtype=torch.bfloat16 if y_bf16 else torch.float32, out_bf16=True)
+    _assert_bit_identical(a, b, w.T * w.k)
+    assert np.array_equal(to_host(ob4), to_host(obf))
+
+
+@pytest.mark.parametrize("E,k,H,I,T,bits,x_dtype", [
+    (16, 4, 96, 64, 3, 2, "bf16"),
+    (8, 2, 4096, 1024, 2, 4, "f32"),
+    (1024, 16, 64, 32, 5, 4, "bf16"),
+    (32, 3, 160, 96, 7, 2, "f32"),
+    (8, 2, 256, 128, 12, 2, "bf16"),
+])
+def test_layer_decode_shapes(moe, E, k, H, I, T, bits, x_dtype):
+    w = _custom(E, k, H, I, T, bits, x_dtype)
+    x, lg, ex = w.x(), w.logits(), w.experts()
+    a, b, _, _ = _four_calls_and_fused(moe, w, x, lg, ex)
+    _assert_bit_identical(a, b, w.T * w.k)
+    ref = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits)
+    assert row_rel_err(to_host(b[4]), ref["out"]) <= DECODE_TOL
+
+
+def test_layer_decode_all_rows_on_two_experts(moe):
+    """Every token routes to the same two experts: 12 rows per expert, several passes."""
+    w = _custom(8, 2, 256, 128, 12, 2)
+    lg = np.tile(np.array([[3.0, 2.0, 0, 0, 0, 0, 0, 0]], np.float32), (w.T, 1))
+    x, ex = w.x(), w.experts()
+    a, b, _, _ = _four_calls_and_fused(moe, w, x, lg, ex)
+    _assert_bit_identical(a, b, w.T * w.k)
+
+
+def test_layer_decode_repeated_calls_reuse_workspace(moe):
+    """Counters are cleared by every call: three calls in a row on one workspace agree."""
+    import torch
+    w = synth.decode_verify()
+    lg = w.logits()
+    ex = routed_experts(w, lg)
+    layer = moe.ExpertLayer(w.E, w.H, w.I, w.bits, to_dev(ex))
+    xd, ld = to_dev_x(w.x()), to_dev(lg)
+    bufs = {"dws": torch.empty(moe.decode_workspace_bytes(layer, w.T, w.k), dtype=torch.uint8, device="cuda")}
+    outs = []
+    for _ in range(3):
+        outs.append(to_host(moe.layer_decode(layer, xd, ld, w.k, bufs=bufs)[4]).copy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
