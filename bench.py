@@ -8,9 +8,9 @@ bf16 activations N(0, 1), fp32 router logits N(0, 1) plus a Zipf(1.1)
 popularity bias.  All inputs are seeded synthetic data (no trained weights).
 
 A step is one pass of the whole layer: route + dispatch + expert FFN +
-combine, issued as moe_layer_decode (three launches: routing and dispatch in one
-workgroup, the gate/up GEMV, the down GEMV with the combine folded in); the
-same step as four separate calls is timed beside it.  Step i uses layer copy i mod --copies (independent allocations of
+combine, issued as moe_layer_decode (four launches: routing, dispatch and the
+per-expert descriptors in one workgroup, the gate/up GEMV, the down GEMV, the
+combine); the same step as four separate calls is timed beside it.  Step i uses layer copy i mod --copies (independent allocations of
 the same layer, 48 by default, about 1 GB of touched weights per cycle) so
 that the 256 MB on-package cache cannot serve one step from the previous one;
 this is the 48-layer stack of the 125B-shaped model with identical weights.
@@ -25,6 +25,11 @@ The JSON line also carries:
   prefill       the 8,192-token prompt-chunk layer on the MFMA path (tokens/s,
                 and the gate/up GEMM against the 2.5 PFLOP/s dense half-precision
                 MFMA peak); --no-prefill skips it.
+
+--workload stack125b runs decode steps through a 48-layer x 512-expert stack
+(fully resident, then through a 4,096-slot resident-expert table with misses
+copied from page-locked host memory); --workload sweep runs the 40-layer
+4-bit stack at T = 1, 2, 4, 8.  Each prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -40,6 +45,31 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+# Memory traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two runs), scaled
+# by what the same counters read for a plain 256 MiB device-to-device copy in the same runs (FETCH_SIZE reads
+# 131,088 KiB for it: x1.99975; WRITE_SIZE reads 262,144 KiB: x1.0).  Each entry is valid only for the kernel
+# source it was measured on (first 16 hex digits of its SHA-256); after a change the traffic is reported null.
+FETCH_SCALE = 262144.0 / 131088.1875
+WRITE_SCALE = 1.0
+TRAFFIC = {
+    "gemv_gateup": {"source": "ffn_gemv.hip", "sha": "5163141f79130649", "fetch_kib": 7428.3, "write_kib": 120.0},
+    "mfma_gateup": {"source": "ffn_mfma.hip", "sha": "451ba60e1e9a1b97", "fetch_kib": 1296275.2,
+                    "write_kib": 86762.3},
+}
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the counter runs, or None if its source has changed since."""
+    import hashlib
+    t = TRAFFIC.get(kernel)
+    if t is None:
+        return None
+    src = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", t["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != t["sha"]:
+            return None
+    return (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0
 METRIC = "MoE-layer tokens/s (decode T=1–3, prefill 8192) + % of HBM / MFMA roofline"
 
 
@@ -167,7 +197,7 @@ def decode_bench(args, torch, moe, synth, oracle):
         raise SystemExit("bench: the four-call step differs from the fused step")
 
     # dominant kernel: the gate/up GEMV (two thirds of the bytes); the down
-    # kernel (with the folded combine) is timed on alternate steps
+    # kernel is timed on alternate steps
     nprof = 2 * max(NL, 96)
     timer = KernelTimer(nprof)
     for i in range(nprof):
@@ -197,7 +227,7 @@ def decode_bench(args, torch, moe, synth, oracle):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("gemv_gateup"),
             "kernel": "ffn_gateup_kernel (expert gate/up dequant-GEMV + SwiGLU)",
             "bytes_per_launch": gu_bytes,
             "mean_us": gu_ms * 1e3,
@@ -285,13 +315,237 @@ def prefill_bench(args, torch, moe, synth, oracle):
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic("mfma_gateup"),
             "kernel": "mfma_ffn_kernel gate/up (fp16 MFMA, weights decoded in LDS)",
             "flops_per_launch": gu_flops,
             "mean_us": gu_ms * 1e3,
             "down_mean_us": dn_ms * 1e3,
             "down_tflops": dn_flops / (dn_ms * 1e-3) / 1e12,
         },
+    }
+
+
+# ---- stacks of layers (decode steps through many layers) ------------------------------------
+
+def _placed_stack(torch, synth, w, dev, nthreads):
+    """Device-resident [L, E, expert_bytes] stack: a pool of E generated expert blobs (layer 0's), and
+    every (layer, expert) at its own address holding pool[perm_l(e)] for a fixed per-layer permutation."""
+    import numpy as np
+    pool = w.experts(0, nthreads=nthreads)
+    pool_d = torch.from_numpy(pool).to(dev)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 0x5EED))
+    perms = [np.arange(w.E)] + [rng.permutation(w.E) for _ in range(w.layers - 1)]
+    big = torch.empty((w.layers, w.E, w.expert_bytes), dtype=torch.uint8, device=dev)
+    for l in range(w.layers):
+        torch.index_select(pool_d, 0, torch.from_numpy(perms[l]).to(dev), out=big[l])
+    del pool_d
+    return big, pool, perms
+
+
+def _stack_inputs(torch, synth, w, steps, sigma, dev):
+    """x [steps, L, T, H] bf16 (a seeded input for every step and layer: chaining the layers through the residual
+    makes these synthetic activations grow without bound) and logits [steps, L, T, E] fp32 on the device, plus the
+    per-(step, layer) count of unique routed experts (numpy top-k on the same logits; ties are immaterial here)."""
+    import numpy as np
+    xs = np.stack([np.stack([w.x(l, s) for l in range(w.layers)]) for s in range(steps)])
+    lg = np.empty((steps, w.layers, w.T, w.E), np.float32)
+    for l in range(w.layers):
+        walk = synth.drift_walk(w, l, steps, sigma) if sigma > 0 else np.repeat(w.bias(l)[None], steps, 0)
+        for s in range(steps):
+            lg[s, l] = synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, l, s), w.T, w.E, walk[s])
+    top = np.argpartition(-lg, w.k - 1, axis=-1)[..., :w.k]
+    U = np.array([[len(np.unique(top[s, l])) for l in range(w.layers)] for s in range(steps)])
+    x_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+    return x_d, torch.from_numpy(lg).to(dev), U, xs, lg
+
+
+def _check_layers(w):
+    return sorted({0, w.layers // 2, w.layers - 1})
+
+
+def _resident_stack_run(torch, moe, w, big, x_d, lg_d, steps, chunk):
+    """Every step through all layers with moe_layer_decode (residual = the layer input, bf16 output of every
+    (step, layer) kept); graphs of `chunk` steps.  Returns (seconds per step, bf16 outputs [steps, L, T, H],
+    fp32 outputs of step 0 at the check layers)."""
+    dev = big.device
+    L, E, T, k, H = w.layers, w.E, w.T, w.k, w.H
+    eb = w.expert_bytes
+    layers = [moe.ExpertLayer(E, H, w.I, w.bits, big, eb, base_offset=l * E * eb) for l in range(L)]
+    bufs = {
+        "ids": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "dispatch": moe.Dispatch(T, k, E, dev),
+        "y": torch.empty((T, k, H), dtype=torch.float32, device=dev),
+        "out": torch.empty((T, H), dtype=torch.float32, device=dev),
+        "dws": torch.empty(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8, device=dev),
+    }
+    rec = torch.empty((steps, L, T, H), dtype=torch.bfloat16, device=dev)
+    out0 = {l: torch.empty((T, H), dtype=torch.float32, device=dev) for l in _check_layers(w)}
+
+    def run(s, keep=None):
+        for l in range(L):
+            moe.layer_decode(layers[l], x_d[s, l], lg_d[s, l], k, residual=x_d[s, l], out_bf16=rec[s, l], bufs=bufs)
+            if keep is not None and l in keep:
+                keep[l].copy_(bufs["out"])
+
+    check_steps = sorted({0, 1, steps - 1})
+    for s in check_steps:
+        run(s, out0 if s == 0 else None)
+    torch.cuda.synchronize()
+    eager = {s: rec[s].clone() for s in check_steps}
+    cap = torch.cuda.Stream()
+    graphs = []
+    for c0 in range(0, steps, chunk):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for s in range(c0, min(steps, c0 + chunk)):
+                run(s)
+        graphs.append(g)
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    for s, f in eager.items():
+        if not torch.equal(rec[s].view(torch.int16), f.view(torch.int16)):
+            raise SystemExit(f"bench: graph replay of stack step {s} differs from the eager step")
+    return sec, rec, out0
+
+
+def _check_against_oracle(oracle, w, pool, perms, xs, lg, out0, tol=2e-3):
+    """Step 0 at the check layers: fp32 layer outputs against the oracle on the same bytes."""
+    import numpy as np
+    worst = 0.0
+    for l, o in out0.items():
+        ex = pool[perms[l]]
+        res = (xs[0, l].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ref = oracle.layer(xs[0, l], lg[0, l], ex, w.k, w.H, w.I, w.bits, residual=res, want_y=False)
+        got = o.cpu().numpy().astype(np.float64)
+        err = float((np.abs(got - ref["out"]).max(axis=1) / np.abs(ref["out"] - res).max(axis=1)).max())
+        if err > tol:
+            raise SystemExit(f"bench: stack layer {l} does not match the oracle (row error {err:.3e})")
+        worst = max(worst, err)
+    return worst
+
+
+def stack125b_bench(args, torch, moe, synth, oracle):
+    """48 layers x 512 experts, T=3, Zipf(1.2) routing with per-step drift: fully resident, then through a
+    4,096-slot resident-expert table with misses copied from page-locked host memory."""
+    import numpy as np
+    w = synth.stack125b()
+    steps = args.stack_steps or w.extra["steps"]
+    sigma, n_slots = w.extra["drift_sigma"], w.extra["slots"]
+    dev = torch.device("cuda:0")
+    L, E, T, k, H, eb = w.layers, w.E, w.T, w.k, w.H, w.expert_bytes
+    t0 = time.time()
+    big, pool, perms = _placed_stack(torch, synth, w, dev, synth.default_threads())
+    x_d, lg_d, U, xs, lg = _stack_inputs(torch, synth, w, steps, sigma, dev)
+    print(f"[stack125b] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    sec, rec, out0 = _resident_stack_run(torch, moe, w, big, x_d, lg_d, steps, args.stack_chunk)
+    err = _check_against_oracle(oracle, w, pool, perms, xs, lg, out0)
+    ref_rec = rec.view(torch.int16).cpu()
+    del rec
+    algo = float(U.mean()) * L * eb
+    resident = {"us_per_step": sec * 1e6, "stack_tokens_per_s": T / sec, "layer_tokens_per_s": T * L / sec,
+                "algorithmic_GBs": algo / sec / 1e9, "hbm_frac": algo / sec / 1e9 / HBM_PEAK_GBS,
+                "mean_unique_experts_per_layer": float(U.mean()), "checked_layers_row_err": err}
+    print(f"[stack125b] resident: {sec * 1e6:.1f} us/step", file=sys.stderr, flush=True)
+
+    # slot-table mode: page-locked host master copy, 4,096 device slots
+    host = torch.empty((L, E, eb), dtype=torch.uint8, pin_memory=True)
+    host.copy_(big)
+    del big
+    torch.cuda.empty_cache()
+    probe = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    hsrc = host.view(-1)[: 1 << 30]
+    probe.copy_(hsrc, non_blocking=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(3):
+        probe.copy_(hsrc, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_gbs = 3 * (1 << 30) / (time.perf_counter() - t1) / 1e9
+    del probe
+    slots = torch.empty((n_slots, eb), dtype=torch.uint8, device=dev)
+    smap = torch.empty(L * E, dtype=torch.int32, device=dev)
+    table = moe.SlotTable(L, E, n_slots, eb, host, slots, smap)
+    b0 = np.stack([w.bias(l) for l in range(L)]).reshape(-1)
+    hot = np.lexsort((np.arange(L * E), -b0))[:n_slots]  # hottest by step-0 bias, ties to the lower (layer, expert)
+    table.preload([(int(i) // E, int(i) % E) for i in hot])
+    torch.cuda.synchronize()
+    base = table.stats()
+    views = [table.layer(l, H, w.I, w.bits) for l in range(L)]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+    d = moe.Dispatch(T, k, E, dev)
+    y = torch.empty((T, k, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(views[0].workspace_bytes(T, k, "gemv"), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    rec = torch.empty((steps, L, T, H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(steps):
+        for l in range(L):
+            moe.route_topk(lg_d[s, l], k, ids=ids, w=wt)
+            moe.dispatch(ids, E, out=d)
+            table.resolve(l, d)
+            moe.expert_ffn_q(views[l], x_d[s, l], k, d, y=y, path="gemv", ws=ws)
+            moe.combine(y, wt, residual=x_d[s, l], out=out, out_bf16=rec[s, l])
+    torch.cuda.synchronize()
+    sec_s = (time.perf_counter() - t1) / steps
+    st = table.stats()
+    table.close()
+    got = rec.view(torch.int16).cpu()
+    if not torch.equal(got, ref_rec):
+        bad = [s for s in range(steps) if not torch.equal(got[s], ref_rec[s])]
+        raise SystemExit(f"bench: the slot-table stack differs from the resident stack at {len(bad)} of {steps} "
+                         f"steps (first {bad[:5]}); stats {st}")
+    hits, misses = st["hits"] - base["hits"], st["misses"] - base["misses"]
+    h2d = st["bytes_h2d"] - base["bytes_h2d"]
+    slot = {"us_per_step": sec_s * 1e6, "stack_tokens_per_s": T / sec_s, "hit_rate": hits / max(1, hits + misses),
+            "misses_per_step": misses / steps, "h2d_MB_per_step": h2d / steps / 1e6,
+            "h2d_link_GBs_measured": h2d_gbs,
+            "h2d_time_share": (h2d / steps / (h2d_gbs * 1e9)) / sec_s,
+            "bit_identical_to_resident": True,
+            "note": "eager: the host waits for each layer's routing before resolving it"}
+    return {
+        "metric": "MoE stack tokens/s (125B-shaped stack, decode T=3)",
+        "workload": f"48 layers x 512 experts, top-10, hidden 2048, intermediate 512, T=3, 2-bit, Zipf(1.2) routing "
+                    f"with per-step drift 0.05, {steps} steps; {n_slots}-slot table for the slot mode",
+        "unit": "tokens/s", "steps": steps, "resident": resident, "slots": slot,
+        "data": "synthetic; a pool of 512 generated experts placed at every (layer, expert) address under "
+                "per-layer permutations",
+    }
+
+
+def sweep_bench(args, torch, moe, synth, oracle):
+    """40 layers x 256 experts, 4-bit, T in {1, 2, 4, 8}: decode steps through the stack."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    w1 = synth.decode_sweep(1)
+    steps = args.stack_steps or 64
+    big, pool, perms = _placed_stack(torch, synth, w1, dev, synth.default_threads())
+    rows = []
+    for T in (1, 2, 4, 8):
+        w = synth.decode_sweep(T)
+        x_d, lg_d, U, xs, lg = _stack_inputs(torch, synth, w, steps, 0.0, dev)
+        sec, rec, out0 = _resident_stack_run(torch, moe, w, big, x_d, lg_d, steps, args.stack_chunk)
+        err = _check_against_oracle(oracle, w, pool, perms, xs, lg, out0)
+        del rec
+        algo = float(U.mean()) * w.layers * w.expert_bytes
+        rows.append({"T": T, "us_per_step": sec * 1e6, "stack_tokens_per_s": T / sec,
+                     "algorithmic_GBs": algo / sec / 1e9, "hbm_frac": algo / sec / 1e9 / HBM_PEAK_GBS,
+                     "mean_unique_experts_per_layer": float(U.mean()), "checked_layers_row_err": err})
+        print(f"[sweep] T={T}: {sec * 1e6:.1f} us/step", file=sys.stderr, flush=True)
+    return {
+        "metric": "MoE stack tokens/s (40-layer 4-bit decode sweep)",
+        "workload": f"40 layers x 256 experts, top-8, hidden 2048, intermediate 512, 4-bit, Zipf(1.0), {steps} steps",
+        "unit": "tokens/s", "steps": steps, "per_T": rows,
+        "data": "synthetic; a pool of 256 generated experts placed at every (layer, expert) address under "
+                "per-layer permutations",
     }
 
 
@@ -318,6 +572,13 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-bias", type=float, default=1.0, help="scale of the Zipf(1.1) router bias")
+    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep"], default="layer",
+                    help="layer: the decode/verify layer (+ prefill), the default; stack125b / sweep: decode "
+                         "steps through a 48- or 40-layer stack, printed as their own JSON line")
+    ap.add_argument("--stack-steps", type=int, default=0, help="steps of a stack run (default 256 / 64)")
+    ap.add_argument("--stack-chunk", type=int, default=16, help="steps per captured graph in stack runs")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device once (a reference for memory-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -334,6 +595,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.workload != "layer":
+        fn = stack125b_bench if args.workload == "stack125b" else sweep_bench
+        print(json.dumps({**fn(args, torch, moe, synth, oracle), "n_gpus": 1}), flush=True)
+        return
 
     res, data = decode_bench(args, torch, moe, synth, oracle)
     pre = None if args.no_prefill else prefill_bench(args, torch, moe, synth, oracle)

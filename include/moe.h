@@ -254,7 +254,7 @@ typedef enum moe_kernel {
   MOE_KERNEL_ROUTE = 0,
   MOE_KERNEL_DISPATCH = 1,
   MOE_KERNEL_GEMV_GATEUP = 2, /* decode gate/up + SwiGLU */
-  MOE_KERNEL_GEMV_DOWN = 3,   /* decode down (+ the folded combine of moe_layer_decode) */
+  MOE_KERNEL_GEMV_DOWN = 3,   /* decode down GEMV */
   MOE_KERNEL_DECODE_PREP = 7, /* descriptor preparation of the stand-alone GEMV path */
   MOE_KERNEL_MFMA_GATEUP = 4,
   MOE_KERNEL_MFMA_DOWN = 5,

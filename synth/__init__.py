@@ -252,3 +252,13 @@ def drifted_bias(w: Workload, layer: int, step: int, sigma: float) -> np.ndarray
     for s in range(step):
         b = (b + normal_f32(stream_key(w.seed, TAG_DRIFT, layer, s), (w.E,), sigma)).astype(np.float32)
     return b
+
+
+def drift_walk(w: Workload, layer: int, steps: int, sigma: float) -> np.ndarray:
+    """Biases of ``layer`` at steps 0 .. steps-1 as float32 [steps, E]; row s equals drifted_bias(w, layer, s, sigma)."""
+    out = np.empty((steps, w.E), np.float32)
+    b = w.bias(layer).astype(np.float32)
+    for s in range(steps):
+        out[s] = b
+        b = (b + normal_f32(stream_key(w.seed, TAG_DRIFT, layer, s), (w.E,), sigma)).astype(np.float32)
+    return out

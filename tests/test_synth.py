@@ -59,3 +59,11 @@ def test_layer_generation_matches_single_expert_and_threads():
     assert np.array_equal(a[4], synth.expert(0, 2, 4, 64, 32, 2))
     c = synth.layer_experts(0, 2, 6, 64, 32, 2, which=[1, 4])
     assert np.array_equal(c[4], a[4]) and np.array_equal(c[1], a[1]) and not c[0].any()
+
+
+def test_drift_walk_matches_drifted_bias():
+    w = synth.stack125b()
+    walk = synth.drift_walk(w, 3, 6, 0.05)
+    for s in range(6):
+        assert np.array_equal(walk[s], synth.drifted_bias(w, 3, s, 0.05))
+    assert not np.array_equal(walk[0], walk[5])
