@@ -212,8 +212,7 @@ moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void
   if (moe_status st = launch_route_dispatch_decode(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
                                                    active, n_active, W, stream))
     return st;
-  if (moe_status st = launch_ffn_gemv_fused(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, w, residual, r_t,
-                                            out, out_bf16, false, stream))
+  if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, stream))
     return st;
   return launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
 }

@@ -109,13 +109,12 @@ __global__ __launch_bounds__(kBlock) void dispatch_scatter_kernel(const int32_t*
 // Decode step, part 1: route all T tokens (one wave per token, the same
 // routine as the stand-alone routing kernel), dispatch in LDS (the same
 // routine as dispatch_small_kernel), then write the per-expert descriptors the
-// persistent FFN kernel reads and clear its counters.
+// FFN kernels read.
 template <int EPL>
 __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
-    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc,
-    int32_t* __restrict__ done, int32_t* __restrict__ cnt, int n_cnt, int32_t* __restrict__ flag) {
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc) {
   __shared__ dev::DispatchLds L;
   __shared__ int32_t ids_lds[kBlock];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -138,7 +137,6 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
   const int na = *n_active;
   const int max_active = min(E, n);
   for (int s2 = tid; s2 < max_active; s2 += kBlock) {
-    done[s2] = 0;
     if (s2 >= na) continue;
     SlotDesc d;
     d.e = active[s2];
@@ -153,8 +151,6 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
     for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
     desc[s2] = d;
   }
-  for (int i = tid; i < n_cnt; i += kBlock) cnt[i] = 0;
-  if (tid == 0) *flag = 0;
 }
 
 __global__ void dispatch_empty_kernel(int E, int32_t* offsets, int32_t* n_active) {
@@ -180,7 +176,7 @@ moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k
                     : epl <= 8 ? route_dispatch_decode_kernel<8>
                                : route_dispatch_decode_kernel<16>;
   launch_k(MOE_KERNEL_ROUTE, kern, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, ids, w, offsets, sorted_assign,
-           assign_pos, active, n_active, W.desc, W.done, W.cnt, W.n_cnt, W.flag);
+           assign_pos, active, n_active, W.desc);
   return check_launch("route_dispatch_decode");
 }
 

@@ -6,9 +6,8 @@
 // (3)); the fast size is a 2-bit class quantization (section "3. 바로 써먹기").
 //
 // For each active expert e and each of its n_e routed rows x:
-//   g = Wg x, u = Wu x, h = silu(g) * u    (h kept in fp32)
+//   g = Wg x, u = Wu x, h = silu(g) * u    (h kept to about 16 significant bits)
 //   y = Wd h                               (written per assignment)
-// and, in the fused decode step, out[t] = residual[t] + sum_j w[t,j] y[t,j].
 //
 // Arithmetic per block of 32 weights (scale s, min m, codes q):
 //   sum_c (s*q_c + m) x_c = s * sum_c (128 + q_c) x_c + (m - 128*s) * sum_c x_c.
@@ -17,25 +16,33 @@
 // adjacent columns in the two halfwords of a word), and v_dot2c_f32_bf16 does
 // the two MACs against the packed input pair with fp32 accumulation.
 // sum_c x_c is per input row and chunk, computed once per wave.  Inputs that
-// are not bf16 (fp32 activations, the fp32 h) are carried as an unevaluated
-// sum hi + lo of two bf16 values (about 16 significant bits), so the products
+// are not bf16 (fp32 activations, h) are carried as an unevaluated sum
+// hi + lo of two bf16 values (about 16 significant bits), so the products
 // stay exact and accumulation is fp32.
 //
 // Work split.  A row of K weights is cut into K/32 chunks (one scale/min block
-// each).  G lanes share a row (G = gcd(K/32, 64)), each lane owning K/(32G)
-// chunks; a wave covers 64/G rows per step and RL steps, and every lane issues
-// the loads of all its RL rows before any arithmetic.  Lane partial sums are
-// reduced across the G lanes with xor shuffles.  Gate row i and up row i land
-// in the same lane, so SwiGLU is applied right after the reduction.
+// each).  G lanes share a row, each owning K/(32G) chunks; lane partial sums
+// are reduced across the G lanes.
+//
+// Two kernel families:
+//  * wide (H a multiple of 2048 and I a multiple of 512, the shapes of the
+//    decode workloads): gate/up rows are split over all 64 lanes of a wave, so
+//    a lane's activation chunk stays in registers for all its rows; down rows
+//    over 16 lanes.  Activation loads are issued before the weight loads, rows
+//    are consumed in load order, and the lane partials of all (row, token)
+//    pairs are reduced together by a reduce-scatter (each exchange level
+//    halves the values a lane carries: permlane32/16 swaps, then DPP), so the
+//    reduction costs about two instructions per value instead of two per
+//    value and level.  The gate/up kernel writes h as separate bf16 hi and lo
+//    planes for the down kernel.
+//  * general (any H, I that are multiples of 32): G = gcd(K/32, 64), a
+//    butterfly reduction per (row, token), h in fp32.
 //
 // Scheduling.  A decode step moves ~20 MB, a few microseconds of HBM time, so
 // launch and dependency latency dominate.  Every (active expert, row tile) is
-// one workgroup and all of them are resident at once; a per-expert
-// descriptor (id, first row, row count, tokens) built by the preceding
-// single-workgroup kernel lets a workgroup reach its weights and inputs after
-// one dependent load.  In the fused decode step the combine is folded into
-// the down kernel: the workgroup that completes a (token, column tile) cell
-// last sums that cell's k rows into out.
+// one workgroup; a per-expert descriptor (id, first row, row count, tokens)
+// built by the preceding single-workgroup kernel lets a workgroup reach its
+// weights and inputs after one dependent load.
 #include "internal.hpp"
 
 namespace moe {
@@ -107,25 +114,6 @@ __device__ __forceinline__ void load_chunk(XChunk<true>& c, const float* p /* 32
     s = dot2(c.lo[i], 0x3F803F80u, s);
   }
   c.sum = s;
-}
-
-// y rows handed to the workgroup that combines them, inside one launch, are
-// written and read with agent-scope relaxed atomics: plain stores and loads
-// with the agent-coherence bit, so no whole-cache write-back or invalidate is
-// needed.  The hand-off is: every wave waits for its stores to complete, a
-// barrier, then a relaxed counter increment; the last of the k contributors
-// to a cell reads the rows after a barrier.
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(uint16_t* p, uint16_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint16_t ld_coherent(const uint16_t* p) {
-  return __hip_atomic_load(const_cast<uint16_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // (x & m) | c in one VALU op.  gfx950's three-operand encoding takes no
@@ -221,17 +209,11 @@ struct DecodeArgs {
   const int32_t* n_active;
   const SlotDesc* desc;
   const int32_t* sorted_assign;
-  int32_t* done;
-  int32_t* cnt;
-  int32_t* flag;
-  float* h;
+  float* h;       // general kernels: fp32 h [T*k x I]
+  uint16_t* hh;   // wide kernels: bf16 hi plane of h [T*k x I] ...
+  uint16_t* hl;   // ... and lo plane (same bytes as the fp32 h)
   void* y;
-  const float* w;
-  const void* residual;
-  int r_bf16;
-  float* out;
-  uint16_t* out_bf16;
-  int TA, TB;  // gate/up and down items per expert
+  int TA, TB;  // gate/up and down workgroups per expert
   Geo ga, gb;
 };
 
@@ -353,7 +335,7 @@ __device__ __forceinline__ void item_gateup(const DecodeArgs& A, const Slot& d, 
   }
 }
 
-// ---- down -----------------------------------------------------------------------
+// ---- down (general) -------------------------------------------------------------
 template <int BITS, int RL>
 struct DownPre {
   uint32_t code[RL][BITS];
@@ -395,11 +377,9 @@ __device__ __forceinline__ void down_chunk(const DecodeArgs& A, const Slot& d, i
   }
 }
 
-// One pass over the wave's down rows for NT routed rows; chunk 0's weights
-// come from `pre` when have_pre (issued before the wait), the rest are loaded.
-template <int BITS, int NT, int RL, bool YBF16, bool COHERENT>
+template <int BITS, int NT, int RL, bool YBF16>
 __device__ __forceinline__ void down_pass(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int n0,
-                                          int rel0, bool resident, const DownPre<BITS, RL>& pre, bool have_pre) {
+                                          int rel0, bool resident) {
   const int lane = threadIdx.x & 63;
   const int G = A.gb.G, RPI = 64 / G, sl = lane / G, gl = lane % G;
   float part[RL][NT];
@@ -409,14 +389,7 @@ __device__ __forceinline__ void down_pass(const DecodeArgs& A, const Slot& d, co
     for (int t = 0; t < NT; ++t) part[r][t] = 0.f;
 
   if (resident) {
-    if (have_pre) {
-      down_chunk<BITS, NT, RL>(A, d, rel0, 0, pre, part);
-    } else {
-      DownPre<BITS, RL> P;
-      down_load<BITS, RL>(A, blob, n0, 0, P);
-      down_chunk<BITS, NT, RL>(A, d, rel0, 0, P, part);
-    }
-    for (int cc = 1; cc < A.gb.CPL; ++cc) {
+    for (int cc = 0; cc < A.gb.CPL; ++cc) {
       DownPre<BITS, RL> P;
       down_load<BITS, RL>(A, blob, n0, cc, P);
       down_chunk<BITS, NT, RL>(A, d, rel0, cc, P, part);
@@ -437,111 +410,384 @@ __device__ __forceinline__ void down_pass(const DecodeArgs& A, const Slot& d, co
         const int n = n0 + r * RPI + sl;
         if (n >= A.H) continue;
         const float v = resident ? part[r][t] : __builtin_nanf("");
-        if constexpr (YBF16) {
-          const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)v);
-          if constexpr (COHERENT) st_coherent(&reinterpret_cast<uint16_t*>(A.y)[a * A.H + n], b);
-          else reinterpret_cast<uint16_t*>(A.y)[a * A.H + n] = b;
-        } else {
-          if constexpr (COHERENT) st_coherent(&reinterpret_cast<float*>(A.y)[a * A.H + n], v);
-          else reinterpret_cast<float*>(A.y)[a * A.H + n] = v;
-        }
+        if constexpr (YBF16) reinterpret_cast<uint16_t*>(A.y)[a * A.H + n] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        else reinterpret_cast<float*>(A.y)[a * A.H + n] = v;
       }
     }
   }
 }
 
-// Combine one (token, column range) cell: out = residual + sum_j w_j y_j, j ascending.
-template <bool YBF16>
-__device__ __forceinline__ void combine_cell(const DecodeArgs& A, int t, int c0, int c1) {
-  for (int c = c0 + (int)threadIdx.x; c < c1; c += 256) {
-    float acc = 0.f;
-    if (A.residual)
-      acc = A.r_bf16
-                ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(A.residual)[(size_t)t * A.H + c] << 16)
-                : reinterpret_cast<const float*>(A.residual)[(size_t)t * A.H + c];
-    for (int j = 0; j < A.k; ++j) {
-      const float wj = A.w[(size_t)t * A.k + j];
-      const size_t yi = ((size_t)t * A.k + j) * A.H + c;
-      const float yv = YBF16 ? __uint_as_float((uint32_t)ld_coherent(&reinterpret_cast<const uint16_t*>(A.y)[yi]) << 16)
-                             : ld_coherent(&reinterpret_cast<const float*>(A.y)[yi]);
-      acc += wj * yv;
-    }
-    A.out[(size_t)t * A.H + c] = acc;
-    if (A.out_bf16) {
-      uint32_t u = __float_as_uint(acc);
-      u += 0x7FFFu + ((u >> 16) & 1u);
-      A.out_bf16[(size_t)t * A.H + c] = (uint16_t)(u >> 16);
-    }
-  }
-}
-
-template <int BITS, int TM, int RL, bool YBF16, bool COMBINE>
+template <int BITS, int TM, int RL, bool YBF16>
 __device__ __forceinline__ void item_down(const DecodeArgs& A, const Slot& d, int j) {
   const int wave = threadIdx.x >> 6;
   const int RPI = 64 / A.gb.G;
   const int n0 = (j * 4 + wave) * RL * RPI;
+  if (n0 >= A.H) return;
   const int idx = resident_index(A, d.e);
   const bool resident = idx >= 0;
   const uint8_t* blob = A.base + (int64_t)(resident ? idx : 0) * A.stride;
-  if (n0 < A.H) {
-    DownPre<BITS, RL> none;
-    for (int tg = 0; tg < d.ne;) {
-      const int nt = min(d.ne - tg, TM);
-      if (nt >= 4) down_pass<BITS, (TM >= 4 ? 4 : 1), RL, YBF16, COMBINE>(A, d, blob, n0, tg, resident, none, false);
-      else if (nt == 3) down_pass<BITS, (TM >= 3 ? 3 : 1), RL, YBF16, COMBINE>(A, d, blob, n0, tg, resident, none, false);
-      else if (nt == 2) down_pass<BITS, (TM >= 2 ? 2 : 1), RL, YBF16, COMBINE>(A, d, blob, n0, tg, resident, none, false);
-      else down_pass<BITS, 1, RL, YBF16, COMBINE>(A, d, blob, n0, tg, resident, none, false);
-      tg += nt;
-    }
-  }
-
-  if constexpr (COMBINE) {
-    __shared__ int last[kDescT];
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's y stores are complete
-    __syncthreads();
-    if ((int)threadIdx.x < d.ne) {
-      const int t = d.p->tok[threadIdx.x];
-      const int old = __hip_atomic_fetch_add(&A.cnt[t * A.TB + j], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last[threadIdx.x] = (old == A.k - 1) ? t : -1;
-    }
-    __syncthreads();
-    const int c0 = j * 4 * RL * RPI, c1 = min(A.H, c0 + 4 * RL * RPI);
-    for (int q = 0; q < d.ne; ++q)
-      if (last[q] >= 0) combine_cell<YBF16>(A, last[q], c0, c1);
+  for (int tg = 0; tg < d.ne;) {
+    const int nt = min(d.ne - tg, TM);
+    if (nt >= 4) down_pass<BITS, (TM >= 4 ? 4 : 1), RL, YBF16>(A, d, blob, n0, tg, resident);
+    else if (nt == 3) down_pass<BITS, (TM >= 3 ? 3 : 1), RL, YBF16>(A, d, blob, n0, tg, resident);
+    else if (nt == 2) down_pass<BITS, (TM >= 2 ? 2 : 1), RL, YBF16>(A, d, blob, n0, tg, resident);
+    else down_pass<BITS, 1, RL, YBF16>(A, d, blob, n0, tg, resident);
+    tg += nt;
   }
 }
 
-// Gate/up + SwiGLU: one workgroup per (active expert, tile of I).
+// ---- cross-lane reduce-scatter (wave64) --------------------------------------------
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// One exchange level over lane bit BIT.  Lanes with the bit clear return
+// a + a(partner), lanes with the bit set return b + b(partner); the partner
+// differs in that bit.  Bit 5: v_permlane32_swap (swaps the upper half of one
+// register with the lower half of the other), bit 4: v_permlane16_swap (odd
+// 16-lane rows with even ones); bits 3..0 stay inside a 16-lane row: DPP
+// row_ror:8 (lane i <-> i^8), row_half_mirror (i <-> 7-i within 8, which
+// differs from i in bit 2), quad_perm [2,3,0,1] and [1,0,3,2].
+template <int BIT>
+__device__ __forceinline__ float scatter_pair(float a, float b, int lane) {
+  if constexpr (BIT == 5 || BIT == 4) {
+    const u32x2_t r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                               : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r.x) + __uint_as_float(r.y);
+  } else {
+    constexpr int kCtrl = BIT == 3 ? 0x128 : BIT == 2 ? 0x141 : BIT == 1 ? 0x4E : 0xB1;
+    const bool hi = (lane >> BIT) & 1;
+    const float send = hi ? a : b, keep = hi ? b : a;
+    return keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), kCtrl, 0xF, 0xF, false));
+  }
+}
+
+// v + v(partner over lane bit BIT): both lanes of a pair end with the sum.
+template <int BIT>
+__device__ __forceinline__ float butterfly(float v) {
+  if constexpr (BIT == 5 || BIT == 4) {
+    const uint32_t u = __float_as_uint(v);
+    const u32x2_t r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                               : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r.x) + __uint_as_float(r.y);
+  } else {
+    constexpr int kCtrl = BIT == 3 ? 0x128 : BIT == 2 ? 0x141 : BIT == 1 ? 0x4E : 0xB1;
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+  }
+}
+
+// Sums v[0..NV) over the lanes that differ in bits BIT..BOT.  While a lane
+// carries more than KEEP values, each level keeps one half (the first half
+// where the lane's bit is clear); after the last such level the remaining
+// levels are butterflies.  On return v[0..NVf) holds sums, NVf = NV >> S for
+// S = min(log2(NV / KEEP), BIT - BOT + 1) halving levels, and v[i] is value
+// number blk * NVf + i, blk being the lane's bits BIT .. BIT-S+1 read as a
+// binary number (BIT the most significant).
+template <int NV, int KEEP, int BIT, int BOT>
+__device__ __forceinline__ void reduce_scatter(float* v, int lane) {
+  if constexpr (BIT >= BOT) {
+    if constexpr (NV > KEEP) {
+#pragma unroll
+      for (int i = 0; i < NV / 2; ++i) v[i] = scatter_pair<BIT>(v[i], v[i + NV / 2], lane);
+      reduce_scatter<NV / 2, KEEP, BIT - 1, BOT>(v, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = butterfly<BIT>(v[i]);
+      reduce_scatter<NV, KEEP, BIT - 1, BOT>(v, lane);
+    }
+  }
+}
+
+constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// ---- wide kernels: gate/up over 64 lanes, down over 16 lanes ------------------------
+// Raw activation chunk (32 columns) of one token: bf16 (16 packed pairs) or
+// fp32 (32 floats, split later).
+template <bool SPLIT>
+struct RawX {
+  uint32_t w[SPLIT ? 32 : 16];
+};
+
+template <bool SPLIT>
+__device__ __forceinline__ void load_raw(RawX<SPLIT>& r, const void* xin, int64_t tok, int H, int chunk) {
+  const uint4* q = SPLIT ? reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(xin) + tok * H + 32 * chunk)
+                         : reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xin) + tok * H + 32 * chunk);
+#pragma unroll
+  for (int i = 0; i < (SPLIT ? 8 : 4); ++i) {
+    const uint4 v = q[i];
+    r.w[4 * i + 0] = v.x;
+    r.w[4 * i + 1] = v.y;
+    r.w[4 * i + 2] = v.z;
+    r.w[4 * i + 3] = v.w;
+  }
+}
+
+// Same packed pairs and chunk sum as load_chunk, from registers.
+template <bool SPLIT>
+__device__ __forceinline__ void make_chunk(XChunk<SPLIT>& c, const RawX<SPLIT>& r) {
+  float s = 0.f;
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      split_pair(__uint_as_float(r.w[2 * i]), __uint_as_float(r.w[2 * i + 1]), c.hi[i], c.lo[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s = dot2(c.hi[i], 0x3F803F80u, s);
+      s = dot2(c.lo[i], 0x3F803F80u, s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c.hi[i] = r.w[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = dot2(c.hi[i], 0x3F803F80u, s);
+  }
+  c.sum = s;
+}
+
+// I rows (gate and up) per wave of the wide gate/up kernel; rows per lane of
+// the wide down kernel (each step covers 4 rows, one per 16-lane group).
+#ifndef MOE_WIDE_NI
+#define MOE_WIDE_NI 4
+#endif
+#ifndef MOE_WIDE_NI_SPLIT
+#define MOE_WIDE_NI_SPLIT 2
+#endif
+#ifndef MOE_WIDE_RL
+#define MOE_WIDE_RL 4
+#endif
+constexpr int kWideTM = 3;  // routed rows per pass in the wide kernels
+template <bool SPLIT> constexpr int kWideNI = SPLIT ? MOE_WIDE_NI_SPLIT : MOE_WIDE_NI;
+constexpr int kWideRL = MOE_WIDE_RL;
+
+template <int BITS, int NT, bool SPLIT>
+__device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int i0,
+                                                 int rel0) {
+  constexpr int NI = kWideNI<SPLIT>;
+  const int lane = threadIdx.x & 63;
+  const int64_t rcb = (int64_t)A.H * BITS / 8, rsb = (int64_t)(A.H / 32) * 4;
+  int64_t tok[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tok[t] = row_token(A, d, rel0 + t);
+  int64_t ri[NI];
+#pragma unroll
+  for (int r = 0; r < NI; ++r) ri[r] = min(i0 + r, A.I - 1);  // rows past I compute on a valid row, dropped
+
+  float pg[NI][NT], pu[NI][NT];
+#pragma unroll
+  for (int r = 0; r < NI; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pg[r][t] = pu[r][t] = 0.f;
+
+  const int cpl = A.H / 2048;
+  for (int cc = 0; cc < cpl; ++cc) {
+    const int chunk = lane + 64 * cc;
+    RawX<SPLIT> rx[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) load_raw<SPLIT>(rx[t], A.xin, tok[t], A.H, chunk);
+    uint32_t cg[NI][BITS], cu[NI][BITS], sg[NI], su[NI];
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      load_codes<BITS>(cg[r], blob + A.off_gc + ri[r] * rcb + chunk * (4 * BITS));
+      sg[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_gs + ri[r] * rsb + chunk * 4);
+      load_codes<BITS>(cu[r], blob + A.off_uc + ri[r] * rcb + chunk * (4 * BITS));
+      su[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_us + ri[r] * rsb + chunk * 4);
+    }
+    XChunk<SPLIT> xc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) make_chunk<SPLIT>(xc[t], rx[t]);
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      const float s1 = f16lo(sg[r]), m1 = f16hi(sg[r]), s2 = f16lo(su[r]), m2 = f16hi(su[r]);
+      const float mo1 = m1 - 128.0f * s1, mo2 = m2 - 128.0f * s2;
+      // explicit fused multiply-adds: the same operations whatever the pass's row count
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        pg[r][t] = __builtin_fmaf(s1, chunk_dot<BITS, SPLIT>(cg[r], xc[t]), __builtin_fmaf(mo1, xc[t].sum, pg[r][t]));
+        pu[r][t] = __builtin_fmaf(s2, chunk_dot<BITS, SPLIT>(cu[r], xc[t]), __builtin_fmaf(mo2, xc[t].sum, pu[r][t]));
+      }
+    }
+  }
+
+  // value 2m + {0: gate, 1: up} for m = r * NT + t, padded to a power of two
+  constexpr int M = NI * NT, MP = pow2_ceil(M), S = log2_exact(MP);
+  static_assert(S <= 6, "at most 64 (row, token) pairs per wave");
+  float v[2 * MP];
+#pragma unroll
+  for (int m = 0; m < MP; ++m) {
+    v[2 * m] = m < M ? pg[m / NT][m % NT] : 0.f;
+    v[2 * m + 1] = m < M ? pu[m / NT][m % NT] : 0.f;
+  }
+  reduce_scatter<2 * MP, 2, 5, 0>(v, lane);
+  const int m = lane >> (6 - S);
+  if ((lane & ((1 << (6 - S)) - 1)) == 0 && m < M) {
+    const int r = m / NT, t = m % NT, i = i0 + r;
+    if (i < A.I) {
+      const float g = v[0], u = v[1];
+      const float hv = g / (1.0f + expf(-g)) * u;
+      const size_t o = (size_t)(d.p0 + rel0 + t) * A.I + i;
+      const __bf16 hb = (__bf16)hv;
+      A.hh[o] = __builtin_bit_cast(uint16_t, hb);
+      A.hl[o] = __builtin_bit_cast(uint16_t, (__bf16)(hv - (float)hb));
+    }
+  }
+}
+
 template <int BITS, int TM, bool SPLIT>
+__device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot& d, int j) {
+  constexpr int NI = kWideNI<SPLIT>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i0 = (j * 4 + wave) * NI;
+  if (i0 >= A.I) return;
+  const int idx = resident_index(A, d.e);
+  if (idx < 0) {  // expert not resident: poison its h rows
+    if (lane < NI && i0 + lane < A.I)
+      for (int t = 0; t < d.ne; ++t) {
+        const size_t o = (size_t)(d.p0 + t) * A.I + i0 + lane;
+        A.hh[o] = 0x7FC0;  // bf16 quiet NaN
+        A.hl[o] = 0;
+      }
+    return;
+  }
+  const uint8_t* blob = A.base + (int64_t)idx * A.stride;
+  for (int tg = 0; tg < d.ne;) {
+    const int nt = min(d.ne - tg, TM);
+    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT>(A, d, blob, i0, tg);
+    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT>(A, d, blob, i0, tg);
+    else gateup_pass_wide<BITS, 1, SPLIT>(A, d, blob, i0, tg);
+    tg += nt;
+  }
+}
+
+template <int BITS, int NT, bool YBF16>
+__device__ __forceinline__ void down_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int n0,
+                                               int rel0, bool resident) {
+  constexpr int RL = kWideRL;
+  const int lane = threadIdx.x & 63, sl = lane >> 4, gl = lane & 15;
+  const int64_t rcb = (int64_t)A.I * BITS / 8, rsb = (int64_t)(A.I / 32) * 4;
+  float part[RL][NT];
+#pragma unroll
+  for (int r = 0; r < RL; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) part[r][t] = 0.f;
+
+  if (resident) {
+    const int cpl = A.I / 512;
+    for (int cc = 0; cc < cpl; ++cc) {
+      const int chunk = gl + 16 * cc;
+      XChunk<true> hc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const size_t o = (size_t)(d.p0 + rel0 + t) * A.I + 32 * chunk;
+        const uint4* qh = reinterpret_cast<const uint4*>(A.hh + o);
+        const uint4* ql = reinterpret_cast<const uint4*>(A.hl + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 a = qh[i], b = ql[i];
+          hc[t].hi[4 * i + 0] = a.x;
+          hc[t].hi[4 * i + 1] = a.y;
+          hc[t].hi[4 * i + 2] = a.z;
+          hc[t].hi[4 * i + 3] = a.w;
+          hc[t].lo[4 * i + 0] = b.x;
+          hc[t].lo[4 * i + 1] = b.y;
+          hc[t].lo[4 * i + 2] = b.z;
+          hc[t].lo[4 * i + 3] = b.w;
+        }
+      }
+      uint32_t code[RL][BITS], smw[RL];
+#pragma unroll
+      for (int r = 0; r < RL; ++r) {
+        const int64_t n = min(n0 + 4 * r + sl, A.H - 1);
+        load_codes<BITS>(code[r], blob + A.off_dc + n * rcb + chunk * (4 * BITS));
+        smw[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_ds + n * rsb + chunk * 4);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s = dot2(hc[t].hi[i], 0x3F803F80u, s);
+          s = dot2(hc[t].lo[i], 0x3F803F80u, s);
+        }
+        hc[t].sum = s;
+      }
+#pragma unroll
+      for (int r = 0; r < RL; ++r) {
+        const float s = f16lo(smw[r]), m = f16hi(smw[r]);
+        const float mo = m - 128.0f * s;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          part[r][t] = __builtin_fmaf(s, chunk_dot<BITS, true>(code[r], hc[t]), __builtin_fmaf(mo, hc[t].sum, part[r][t]));
+      }
+    }
+  }
+
+  constexpr int M = RL * NT, MP = pow2_ceil(M), S = cmin(log2_exact(MP), 4), NVF = MP >> S;
+  float v[MP];
+#pragma unroll
+  for (int m = 0; m < MP; ++m) v[m] = m < M ? part[m / NT][m % NT] : 0.f;
+  reduce_scatter<MP, 1, 3, 0>(v, lane);
+  if ((gl & ((1 << (4 - S)) - 1)) == 0) {
+    const int blk = gl >> (4 - S);
+#pragma unroll
+    for (int q = 0; q < NVF; ++q) {
+      const int m = blk * NVF + q;
+      if (m >= M) continue;
+      const int r = m / NT, t = m % NT, n = n0 + 4 * r + sl;
+      if (n >= A.H) continue;
+      const int64_t a = row_assign(A, d, rel0 + t);
+      const float val = resident ? v[q] : __builtin_nanf("");
+      if constexpr (YBF16) reinterpret_cast<uint16_t*>(A.y)[a * A.H + n] = __builtin_bit_cast(uint16_t, (__bf16)val);
+      else reinterpret_cast<float*>(A.y)[a * A.H + n] = val;
+    }
+  }
+}
+
+template <int BITS, int TM, bool YBF16>
+__device__ __forceinline__ void item_down_wide(const DecodeArgs& A, const Slot& d, int j) {
+  const int wave = threadIdx.x >> 6;
+  const int n0 = (j * 4 + wave) * 4 * kWideRL;
+  if (n0 >= A.H) return;
+  const int idx = resident_index(A, d.e);
+  const bool resident = idx >= 0;
+  const uint8_t* blob = A.base + (int64_t)(resident ? idx : 0) * A.stride;
+  for (int tg = 0; tg < d.ne;) {
+    const int nt = min(d.ne - tg, TM);
+    if (nt >= 3) down_pass_wide<BITS, (TM >= 3 ? 3 : 1), YBF16>(A, d, blob, n0, tg, resident);
+    else if (nt == 2) down_pass_wide<BITS, (TM >= 2 ? 2 : 1), YBF16>(A, d, blob, n0, tg, resident);
+    else down_pass_wide<BITS, 1, YBF16>(A, d, blob, n0, tg, resident);
+    tg += nt;
+  }
+}
+
+// ---- kernels ----------------------------------------------------------------------
+// Gate/up + SwiGLU: one workgroup per (active expert, tile of I).
+template <int BITS, int TM, bool SPLIT, bool WIDE>
 __global__ __launch_bounds__(256) void ffn_gateup_kernel(DecodeArgs A) {
-  constexpr int RLA = SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>;
   const int s = blockIdx.x / A.TA, j = blockIdx.x % A.TA;
   if (s >= *A.n_active) return;
   const Slot d = load_slot(A, s);
-  item_gateup<BITS, TM, SPLIT, RLA>(A, d, j);
+  if constexpr (WIDE) item_gateup_wide<BITS, TM, SPLIT>(A, d, j);
+  else item_gateup<BITS, TM, SPLIT, SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>>(A, d, j);
 }
 
-// Down (+ combine): one workgroup per (active expert, tile of H).
-template <int BITS, int TM, bool YBF16, bool COMBINE>
+// Down: one workgroup per (active expert, tile of H).
+template <int BITS, int TM, bool YBF16, bool WIDE>
 __global__ __launch_bounds__(256) void ffn_down_kernel(DecodeArgs A) {
-  constexpr int RLB = kRLDown<TM>;
   const int s = blockIdx.x / A.TB, j = blockIdx.x % A.TB;
   if (s >= *A.n_active) return;
   const Slot d = load_slot(A, s);
-  item_down<BITS, TM, RLB, YBF16, COMBINE>(A, d, j);
+  if constexpr (WIDE) item_down_wide<BITS, TM, YBF16>(A, d, j);
+  else item_down<BITS, TM, kRLDown<TM>, YBF16>(A, d, j);
 }
 
-// Descriptors from the dispatch arrays, and counters cleared.
+// Descriptors from the dispatch arrays.
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted_assign,
                                                           const int32_t* __restrict__ active,
                                                           const int32_t* __restrict__ n_active, int k, int max_active,
-                                                          SlotDesc* __restrict__ desc, int32_t* __restrict__ done,
-                                                          int32_t* __restrict__ cnt, int n_cnt,
-                                                          int32_t* __restrict__ flag) {
+                                                          SlotDesc* __restrict__ desc) {
   const int na = *n_active;
   for (int s = threadIdx.x; s < max_active; s += 256) {
-    done[s] = 0;
     if (s >= na) continue;
     SlotDesc d;
     d.e = active[s];
@@ -556,37 +802,53 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restr
     for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
     desc[s] = d;
   }
-  for (int i = threadIdx.x; i < n_cnt; i += 256) cnt[i] = 0;
-  if (threadIdx.x == 0) *flag = 0;
 }
 
-template <int BITS, int TM, bool SPLIT, bool YBF16, bool COMBINE>
-moe_status launch_tm(DecodeArgs& a, int max_active, hipStream_t s) {
-  constexpr int RLA = SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>;
-  constexpr int RLB = kRLDown<TM>;
-  const int NI = RLA * (64 / a.ga.G) / 2;
-  a.TA = (int)ceil_div(a.I, 4 * NI);
-  a.TB = (int)ceil_div(a.H, 4 * RLB * (64 / a.gb.G));
-  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_gateup_kernel<BITS, TM, SPLIT>, dim3((unsigned)(max_active * a.TA)), dim3(256),
-           0, s, a);
+// The wide kernels apply when gate/up rows split over 64 lanes and down rows
+// over 16 lanes in whole 32-column chunks.  One compiled instantiation serves
+// every T (passes of up to kWideTM rows): separately compiled copies of the
+// same pass were seen to round differently, and a token's row must not depend
+// on which other tokens share its step.
+bool wide_shape(int H, int I) { return H % 2048 == 0 && I % 512 == 0; }
+
+template <int BITS, bool SPLIT, bool YBF16>
+moe_status launch_wide(DecodeArgs& a, int max_active, hipStream_t s) {
+  a.TA = (int)ceil_div(a.I, 4 * kWideNI<SPLIT>);
+  a.TB = (int)ceil_div(a.H, 4 * 4 * kWideRL);
+  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_gateup_kernel<BITS, kWideTM, SPLIT, true>,
+           dim3((unsigned)(max_active * a.TA)), dim3(256), 0, s, a);
   if (moe_status st = check_launch("ffn_gateup")) return st;
-  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_kernel<BITS, TM, YBF16, COMBINE>, dim3((unsigned)(max_active * a.TB)),
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_kernel<BITS, kWideTM, YBF16, true>, dim3((unsigned)(max_active * a.TB)),
            dim3(256), 0, s, a);
   return check_launch("ffn_down");
 }
 
-template <int BITS, bool SPLIT, bool YBF16, bool COMBINE>
-moe_status launch_t(DecodeArgs& a, int T, int max_active, hipStream_t s) {
-  if (T <= 1) return launch_tm<BITS, 1, SPLIT, YBF16, COMBINE>(a, max_active, s);
-  if (T <= 2) return launch_tm<BITS, 2, SPLIT, YBF16, COMBINE>(a, max_active, s);
-  if (T <= 3) return launch_tm<BITS, 3, SPLIT, YBF16, COMBINE>(a, max_active, s);
-  return launch_tm<BITS, 4, SPLIT, YBF16, COMBINE>(a, max_active, s);
+template <int BITS, int TM, bool SPLIT, bool YBF16>
+moe_status launch_tm(DecodeArgs& a, int max_active, hipStream_t s) {
+  constexpr int RLA = SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>;
+  constexpr int RLB = kRLDown<TM>;
+  a.TA = (int)ceil_div(a.I, 4 * (RLA * (64 / a.ga.G) / 2));
+  a.TB = (int)ceil_div(a.H, 4 * RLB * (64 / a.gb.G));
+  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_gateup_kernel<BITS, TM, SPLIT, false>, dim3((unsigned)(max_active * a.TA)),
+           dim3(256), 0, s, a);
+  if (moe_status st = check_launch("ffn_gateup")) return st;
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_kernel<BITS, TM, YBF16, false>, dim3((unsigned)(max_active * a.TB)),
+           dim3(256), 0, s, a);
+  return check_launch("ffn_down");
 }
 
-template <bool SPLIT, bool YBF16, bool COMBINE>
+template <int BITS, bool SPLIT, bool YBF16>
+moe_status launch_t(DecodeArgs& a, int T, int max_active, hipStream_t s) {
+  if (wide_shape(a.H, a.I)) return launch_wide<BITS, SPLIT, YBF16>(a, max_active, s);
+  if (T <= 1) return launch_tm<BITS, 1, SPLIT, YBF16>(a, max_active, s);
+  if (T <= 2) return launch_tm<BITS, 2, SPLIT, YBF16>(a, max_active, s);
+  if (T <= 3) return launch_tm<BITS, 3, SPLIT, YBF16>(a, max_active, s);
+  return launch_tm<BITS, 4, SPLIT, YBF16>(a, max_active, s);
+}
+
+template <bool SPLIT, bool YBF16>
 moe_status launch_b(DecodeArgs& a, int bits, int T, int max_active, hipStream_t s) {
-  return bits == 2 ? launch_t<2, SPLIT, YBF16, COMBINE>(a, T, max_active, s)
-                   : launch_t<4, SPLIT, YBF16, COMBINE>(a, T, max_active, s);
+  return bits == 2 ? launch_t<2, SPLIT, YBF16>(a, T, max_active, s) : launch_t<4, SPLIT, YBF16>(a, T, max_active, s);
 }
 
 DecodeArgs make_args(const moe_qlayer& q, const void* x, int T, int k, const int32_t* sorted_assign,
@@ -610,10 +872,9 @@ DecodeArgs make_args(const moe_qlayer& q, const void* x, int T, int k, const int
   a.n_active = n_active;
   a.desc = W.desc;
   a.sorted_assign = sorted_assign;
-  a.done = W.done;
-  a.cnt = W.cnt;
-  a.flag = W.flag;
   a.h = W.h;
+  a.hh = reinterpret_cast<uint16_t*>(W.h);
+  a.hl = a.hh + (size_t)T * k * q.I;
   a.y = y;
   a.ga.G = gcd_pow2_64(q.H / 32);
   a.ga.CPL = (q.H / 32) / a.ga.G;
@@ -625,52 +886,31 @@ DecodeArgs make_args(const moe_qlayer& q, const void* x, int T, int k, const int
 }  // namespace
 
 DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I) {
+  (void)H;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   uint8_t* b = reinterpret_cast<uint8_t*>(ws);
   const int n = T * k, max_active = std::min(E, n);
   DecodeWs W;
   size_t off = 0;
-  W.h = reinterpret_cast<float*>(b + off);
+  W.h = reinterpret_cast<float*>(b + off);  // fp32 h, or the two bf16 planes of the wide kernels
   off += up((size_t)n * I * 4);
   W.desc = reinterpret_cast<SlotDesc*>(b + off);
   off += up((size_t)max_active * sizeof(SlotDesc));
-  W.done = reinterpret_cast<int32_t*>(b + off);
-  off += up((size_t)max_active * 4);
-  W.n_cnt = T * (int)ceil_div(H, 16);
-  W.cnt = reinterpret_cast<int32_t*>(b + off);
-  off += up((size_t)W.n_cnt * 4);
-  W.flag = reinterpret_cast<int32_t*>(b + off);
-  off += 256;
   W.bytes = off;
   return W;
 }
 
 size_t ffn_gemv_ws_bytes(int T, int k, int E, int H, int I) { return decode_ws(nullptr, T, k, E, H, I).bytes; }
 
-moe_status launch_ffn_gemv_fused(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
+moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
-                                 moe_dtype y_t, const float* w, const void* residual, moe_dtype r_t, float* out,
-                                 uint16_t* out_bf16, bool combine, hipStream_t s) {
+                                 moe_dtype y_t, hipStream_t s) {
   DecodeArgs a = make_args(q, x, T, k, sorted_assign, n_active, W, y);
-  a.w = w;
-  a.residual = residual;
-  a.r_bf16 = r_t == MOE_BF16;
-  a.out = out;
-  a.out_bf16 = out_bf16;
   const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
   const bool split = x_t == MOE_F32, yb = y_t == MOE_BF16;
-  if (combine) {
-    if (split)
-      return yb ? launch_b<true, true, true>(a, q.bits, T, max_active, s)
-                : launch_b<true, false, true>(a, q.bits, T, max_active, s);
-    return yb ? launch_b<false, true, true>(a, q.bits, T, max_active, s)
-              : launch_b<false, false, true>(a, q.bits, T, max_active, s);
-  }
   if (split)
-    return yb ? launch_b<true, true, false>(a, q.bits, T, max_active, s)
-              : launch_b<true, false, false>(a, q.bits, T, max_active, s);
-  return yb ? launch_b<false, true, false>(a, q.bits, T, max_active, s)
-            : launch_b<false, false, false>(a, q.bits, T, max_active, s);
+    return yb ? launch_b<true, true>(a, q.bits, T, max_active, s) : launch_b<true, false>(a, q.bits, T, max_active, s);
+  return yb ? launch_b<false, true>(a, q.bits, T, max_active, s) : launch_b<false, false>(a, q.bits, T, max_active, s);
 }
 
 moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
@@ -679,10 +919,9 @@ moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, in
   const DecodeWs W = decode_ws(ws, T, k, q.E, q.H, q.I);
   const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
   launch_k(MOE_KERNEL_DECODE_PREP, decode_prep_kernel, dim3(1), dim3(256), 0, s, offsets, sorted_assign, active,
-           n_active, k, max_active, W.desc, W.done, W.cnt, W.n_cnt, W.flag);
+           n_active, k, max_active, W.desc);
   if (moe_status st = check_launch("decode_prep")) return st;
-  return launch_ffn_gemv_fused(q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, nullptr, nullptr, MOE_F32, nullptr,
-                               nullptr, false, s);
+  return launch_ffn_gemv_steps(q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, s);
 }
 
 }  // namespace moe

@@ -49,15 +49,11 @@ struct SlotDesc {
 };
 static_assert(sizeof(SlotDesc) == 128, "SlotDesc is one 128-byte record");
 
-// Decode workspace: h [T*k x I] fp32, slot descriptors, per-slot gate/up
-// completion counters, per-(token, column tile) combine counters, a flag.
+// Decode workspace: h [T*k x I] (fp32, or bf16 hi and lo planes in the same
+// bytes) and the slot descriptors.
 struct DecodeWs {
   float* h;
   SlotDesc* desc;
-  int32_t* done;
-  int32_t* cnt;
-  int32_t* flag;
-  int n_cnt;
   size_t bytes;
 };
 DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I);
@@ -67,15 +63,14 @@ moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, in
                            const int32_t* sorted_assign, const int32_t* active, const int32_t* n_active, void* y,
                            moe_dtype y_t, void* ws, hipStream_t s);
 
-// Fused decode step: route + dispatch + descriptors in one workgroup, then the
-// persistent FFN kernel with the combine folded in.
+// Decode step: route + dispatch + descriptors in one workgroup, then the
+// gate/up and down kernels reading the descriptors.
 moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                                         int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
                                         int32_t* active, int32_t* n_active, const DecodeWs& W, hipStream_t s);
-moe_status launch_ffn_gemv_fused(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
+moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
-                                 moe_dtype y_t, const float* w, const void* residual, moe_dtype r_t, float* out,
-                                 uint16_t* out_bf16, bool combine, hipStream_t s);
+                                 moe_dtype y_t, hipStream_t s);
 
 size_t ffn_mfma_ws_bytes(int T, int k, int E, int H, int I);
 moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
