@@ -22,9 +22,14 @@ SOURCES = ["api.hip", "route_topk.hip", "dispatch.hip", "ffn_gemv.hip", "ffn_mfm
            "slot_table.hip"]
 
 ARCH = "gfx950"
-# Packed fp32 VALU ops are disabled for all device code.
+# Packed fp32 VALU ops are disabled for all device code.  Floating-point
+# contraction is off: a multiply and an add are fused only where the source asks
+# for it (__builtin_fmaf).  With contraction left to the compiler, two compiled
+# instances of the same code (e.g. kernels specialised for different token
+# counts) were measured to round differently, which breaks bit-identical results
+# between entry points that share arithmetic.
 CFLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+          "-packed-fp32-ops", "-ffp-contract=off", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def hipcc() -> str:

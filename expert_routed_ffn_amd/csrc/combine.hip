@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, 
     const float wj = w[(size_t)t * k + j];
     const F4 v = load4(y + ((size_t)t * k + j) * H + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc.v[i] += wj * v.v[i];
+    for (int i = 0; i < 4; ++i) acc.v[i] = __builtin_fmaf(wj, v.v[i], acc.v[i]);
   }
   *reinterpret_cast<float4*>(out + (size_t)t * H + c) = make_float4(acc.v[0], acc.v[1], acc.v[2], acc.v[3]);
   if (out_bf16) {

@@ -285,7 +285,8 @@ __device__ __forceinline__ void gateup_pass(const DecodeArgs& A, const Slot& d, 
       const float s = f16lo(smw[r]), m = f16hi(smw[r]);
       const float mo = m - 128.0f * s;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) part[r][t] += s * chunk_dot<BITS, SPLIT>(code[r], xc[t]) + mo * xc[t].sum;
+      for (int t = 0; t < NT; ++t)
+        part[r][t] = __builtin_fmaf(s, chunk_dot<BITS, SPLIT>(code[r], xc[t]), __builtin_fmaf(mo, xc[t].sum, part[r][t]));
     }
   }
 
@@ -373,7 +374,8 @@ __device__ __forceinline__ void down_chunk(const DecodeArgs& A, const Slot& d, i
     const float s = f16lo(P.smw[r]), m = f16hi(P.smw[r]);
     const float mo = m - 128.0f * s;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) part[r][t] += s * chunk_dot<BITS, true>(P.code[r], hc[t]) + mo * hc[t].sum;
+    for (int t = 0; t < NT; ++t)
+      part[r][t] = __builtin_fmaf(s, chunk_dot<BITS, true>(P.code[r], hc[t]), __builtin_fmaf(mo, hc[t].sum, part[r][t]));
   }
 }
 
@@ -599,7 +601,6 @@ __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot
     for (int r = 0; r < NI; ++r) {
       const float s1 = f16lo(sg[r]), m1 = f16hi(sg[r]), s2 = f16lo(su[r]), m2 = f16hi(su[r]);
       const float mo1 = m1 - 128.0f * s1, mo2 = m2 - 128.0f * s2;
-      // explicit fused multiply-adds: the same operations whatever the pass's row count
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         pg[r][t] = __builtin_fmaf(s1, chunk_dot<BITS, SPLIT>(cg[r], xc[t]), __builtin_fmaf(mo1, xc[t].sum, pg[r][t]));
@@ -764,8 +765,8 @@ __device__ __forceinline__ void item_down_wide(const DecodeArgs& A, const Slot& 
 template <int BITS, int TM, bool SPLIT, bool WIDE>
 __global__ __launch_bounds__(256) void ffn_gateup_kernel(DecodeArgs A) {
   const int s = blockIdx.x / A.TA, j = blockIdx.x % A.TA;
-  if (s >= *A.n_active) return;
   const Slot d = load_slot(A, s);
+  if (d.e < 0) return;  // slot past the active experts
   if constexpr (WIDE) item_gateup_wide<BITS, TM, SPLIT>(A, d, j);
   else item_gateup<BITS, TM, SPLIT, SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>>(A, d, j);
 }
@@ -774,13 +775,13 @@ __global__ __launch_bounds__(256) void ffn_gateup_kernel(DecodeArgs A) {
 template <int BITS, int TM, bool YBF16, bool WIDE>
 __global__ __launch_bounds__(256) void ffn_down_kernel(DecodeArgs A) {
   const int s = blockIdx.x / A.TB, j = blockIdx.x % A.TB;
-  if (s >= *A.n_active) return;
   const Slot d = load_slot(A, s);
+  if (d.e < 0) return;  // slot past the active experts
   if constexpr (WIDE) item_down_wide<BITS, TM, YBF16>(A, d, j);
   else item_down<BITS, TM, kRLDown<TM>, YBF16>(A, d, j);
 }
 
-// Descriptors from the dispatch arrays.
+// Descriptors from the dispatch arrays (e = -1 for slots past n_active).
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ sorted_assign,
                                                           const int32_t* __restrict__ active,
@@ -788,11 +789,10 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restr
                                                           SlotDesc* __restrict__ desc) {
   const int na = *n_active;
   for (int s = threadIdx.x; s < max_active; s += 256) {
-    if (s >= na) continue;
     SlotDesc d;
-    d.e = active[s];
-    d.p0 = offsets[d.e];
-    d.ne = offsets[d.e + 1] - d.p0;
+    d.e = s < na ? active[s] : -1;
+    d.p0 = s < na ? offsets[d.e] : 0;
+    d.ne = s < na ? offsets[d.e + 1] - d.p0 : 0;
     d.pad = 0;
     for (int j = 0; j < kDescT; ++j) {
       const int a = j < d.ne ? sorted_assign[d.p0 + j] : 0;

@@ -5,11 +5,10 @@
 // Routing (Strata feature, tech.hub77a.com, summary row "핵심 기법" and
 // section "2. 왜 대단한가" (1)-(2)): per token the k largest logits, descending,
 // ties to the lower expert id, -0.0 == +0.0; weights = softmax over the k.
-// Each logit becomes a 64-bit key whose integer order is the ranking order
-// (float mapped to offset binary in the high word, ~id in the low word), so
-// the selection is exact integer work.  A wave owns one token; k rounds of
-// "lane max, then wave max" find the keys.  The wave max runs on DPP lane
-// swaps inside rows of 16 and on readlane across the four rows, all on-chip.
+// Each logit becomes a 32-bit key whose integer order is the float order
+// (offset binary), so the selection is exact integer work.  A wave owns one
+// token; k rounds of "lane max, wave max, lowest id holding it" find the
+// experts, all in registers.
 //
 // Dispatch (section "2. 왜 대단한가" (2): the compute path follows the
 // routing): a stable counting sort of the assignments by expert.
@@ -20,44 +19,39 @@
 namespace moe {
 namespace dev {
 
-__device__ __forceinline__ uint64_t rank_key(float f, int e) {
+// Order key of a logit: integer order equals the float order, -0.0 == +0.0,
+// and 0 lies below every finite logit (used for "taken" and "no expert").
+__device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) == 0) u = 0;  // -0.0 -> +0.0
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)e);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
+__device__ __forceinline__ float key_logit(uint32_t ord) {
   const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+typedef unsigned int u32x2_dev_t __attribute__((ext_vector_type(2)));
 
-// 64-bit value from another lane of the same 16-lane row through a DPP pattern.
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
-// Maximum over the 64 lanes, returned in every lane (wave-uniform).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror: lane i <-> 7-i within 8
-  v = umax64(v, dpp64<0x140>(v));  // row_mirror: lane i <-> 15-i within 16
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  uint64_t m = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t rv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-    m = umax64(m, rv);
-  }
-  return m;
+// Maximum over the 64 lanes, uniform: DPP inside each 16-lane row (quad
+// swaps, half-row and row mirrors), then the permlane16 / permlane32 swaps
+// across rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp32<0x140>(v));  // row_mirror
+  const u32x2_dev_t a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a.x, a.y);
+  const u32x2_dev_t b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(b.x, b.y);
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -67,32 +61,49 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 // One token's routing by one wave.  Lane j < k returns the j-th selected id
-// in *id and its weight in *wt; other lanes return id = -1.
+// in *id and its weight in *wt; other lanes return id = -1.  Expert e sits in
+// lane e % 64, slot e / 64.  Each round takes the wave maximum of the keys,
+// then the lowest expert id holding it (the smallest slot with a match, then
+// the lowest lane: ballots over the slots), and clears that one key.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int& id, float& wt) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[EPL];
+  // all loads first (clamped index, no branch around them), then the keys
+  float lv[EPL];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = (e < E) ? rank_key(row[e], e) : 0ull;  // 0 is below every real key
-  }
-  uint64_t mine = 0;
+  for (int j = 0; j < EPL; ++j) lv[j] = row[min(lane + 64 * j, E - 1)];
+  uint32_t key[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) key[j] = (lane + 64 * j < E) ? order_key(lv[j]) : 0u;
+  uint32_t mine = 0;
+  int mine_id = -1;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
+    uint32_t lm = key[0];
 #pragma unroll
-    for (int j = 1; j < EPL; ++j) best = umax64(best, key[j]);
-    best = wave_max_u64(best);
+    for (int j = 1; j < EPL; ++j) lm = max(lm, key[j]);
+    const uint32_t m = wave_max_u32(lm);
+    int jw = 0, lw = 0;
+#pragma unroll
+    for (int j = EPL - 1; j >= 0; --j) {
+      const uint64_t b = __ballot(key[j] == m);
+      if (b) {
+        jw = j;
+        lw = __builtin_ctzll(b);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      if (key[j] == best) key[j] = 0;
-    if (lane == r) mine = best;
+      if (j == jw && lane == lw) key[j] = 0u;
+    if (lane == r) {
+      mine = m;
+      mine_id = jw * 64 + lw;
+    }
   }
   const float lj = key_logit(mine);
   const float l0 = __shfl(lj, 0, 64);
   const float ex = (lane < k) ? expf(lj - l0) : 0.0f;
   const float den = wave_sum_f32(ex);
-  id = (lane < k) ? (int32_t)(~(uint32_t)mine) : -1;
+  id = (lane < k) ? mine_id : -1;
   wt = (lane < k) ? ex / den : 0.0f;
 }
 
