@@ -212,9 +212,18 @@ moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void
   if (moe_status st = launch_route_dispatch_decode(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
                                                    active, n_active, W, stream))
     return st;
-  if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, stream))
+  FoldedCombine fc;
+  const bool fold = gemv_folds_combine(q->H, q->I);
+  if (fold) {
+    fc.w = w;
+    fc.residual = residual;
+    fc.r_t = r_t;
+    fc.out = out;
+    fc.out_bf16 = out_bf16;
+  }
+  if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, fc, stream))
     return st;
-  return launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
+  return fold ? MOE_OK : launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
 }
 
 moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,

@@ -114,9 +114,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_scatter_kernel(const int32_t*
 // position of assignment a is the number of assignments before it in
 // (expert, index) order; an assignment that is the first of its expert opens
 // an active slot, numbered by the count of such first assignments with a lower
-// expert id.  Every output of moe_dispatch is written, and one descriptor per
+// expert id.  Every output of moe_dispatch is written, one descriptor per
 // slot (expert, first position, row count, tokens, assignments; e = -1 for
-// slots past n_active) for the FFN kernels.
+// slots past n_active) and the (expert, assignment) pair of every sorted
+// position for the FFN kernels.
 constexpr int kDecodeMaxN = kDescT * kMaxK;  // 192
 
 // Counts over the n ids in LDS (padded with kNoId to a multiple of 8), eight
@@ -143,7 +144,8 @@ template <int EPL>
 __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
-    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc, int max_active) {
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc, int max_active,
+    int32_t* __restrict__ rows, int32_t* __restrict__ nrows) {
   __shared__ __align__(16) int32_t s_id[kDecodeMaxN];
   __shared__ __align__(16) int32_t s_first_e[kDecodeMaxN];  // expert id if the first of its expert, else kNoId
   __shared__ int32_t s_sorted[kDecodeMaxN];
@@ -212,6 +214,12 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
     }
   }
   __syncthreads();
+  if (tid < n) {
+    const int a = s_sorted[tid];
+    rows[2 * tid] = s_id[a];
+    rows[2 * tid + 1] = a;
+  }
+  if (tid == 0) *nrows = n;
   const int na = s_na;
   for (int s2 = tid; s2 < max_active; s2 += kBlock) {
     SlotDesc d;
@@ -253,7 +261,7 @@ moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k
                                : route_dispatch_decode_kernel<16>;
   if (T * k > kDecodeMaxN) return fail(MOE_EUNSUPPORTED, "route_dispatch_decode: T*k above 192");
   launch_k(MOE_KERNEL_ROUTE, kern, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, ids, w, offsets, sorted_assign,
-           assign_pos, active, n_active, W.desc, std::min(E, T * k));
+           assign_pos, active, n_active, W.desc, std::min(E, T * k), W.rows, W.nrows);
   return check_launch("route_dispatch_decode");
 }
 

@@ -213,6 +213,14 @@ struct DecodeArgs {
   uint16_t* hh;   // wide kernels: bf16 hi plane of h [T*k x I] ...
   uint16_t* hl;   // ... and lo plane (same bytes as the fp32 h)
   void* y;
+  const int32_t* rows;   // (expert, assignment) per sorted position
+  const int32_t* nrows;  // number of sorted positions
+  // combine folded into the row-tiled down kernel (out == nullptr: not folded)
+  const float* w;
+  const void* residual;
+  int r_bf16;
+  float* out;
+  uint16_t* out_bf16;
   int TA, TB;  // gate/up and down workgroups per expert
   Geo ga, gb;
 };
@@ -760,6 +768,152 @@ __device__ __forceinline__ void item_down_wide(const DecodeArgs& A, const Slot& 
   }
 }
 
+// ---- row-tiled down with the combine folded in ------------------------------------
+// One 1024-thread workgroup owns kRowTile output rows of H.  Its 16 waves take
+// the routed rows (sorted positions: one expert and one assignment each), up
+// to two at a time per wave, over the tile's rows (two steps of 4 rows, 16
+// lanes per row); the y values of the tile go to global memory and to LDS, and
+// the workgroup then forms out[t] = residual[t] + sum_j w[t,j] y[t,j] for its
+// rows with the same fused multiply-add chain as the combine kernel.  No
+// workgroup depends on another.
+constexpr int kRowTile = 8;
+constexpr int kRowWaves = 16;
+constexpr int kDecodeMaxRows = kDescT * kMaxK;  // routed rows a folded combine can hold (192)
+
+template <int BITS, int NIT, bool YBF16>
+__device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (&pp)[NIT], int n0, float* ylds) {
+  const int lane = threadIdx.x & 63, sl = lane >> 4, gl = lane & 15;
+  const int64_t rcb = (int64_t)A.I * BITS / 8, rsb = (int64_t)(A.I / 32) * 4;
+  int aa[NIT];
+  bool res[NIT];
+  int64_t pr[NIT];
+  const uint8_t* blob[NIT];
+#pragma unroll
+  for (int q = 0; q < NIT; ++q) {
+    pr[q] = pp[q] >= 0 ? pp[q] : 0;
+    const int e = A.rows[2 * pr[q]];
+    aa[q] = A.rows[2 * pr[q] + 1];
+    const int idx = resident_index(A, e);
+    res[q] = idx >= 0;
+    blob[q] = A.base + (int64_t)(res[q] ? idx : 0) * A.stride;
+  }
+  float part[NIT][2];
+#pragma unroll
+  for (int q = 0; q < NIT; ++q) part[q][0] = part[q][1] = 0.f;
+  const int cpl = A.I / 512;
+  for (int cc = 0; cc < cpl; ++cc) {
+    const int chunk = gl + 16 * cc;
+    XChunk<true> hc[NIT];
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+      const size_t o = (size_t)pr[q] * A.I + 32 * chunk;
+      const uint4* qh = reinterpret_cast<const uint4*>(A.hh + o);
+      const uint4* ql = reinterpret_cast<const uint4*>(A.hl + o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = qh[i], v = ql[i];
+        hc[q].hi[4 * i + 0] = u.x;
+        hc[q].hi[4 * i + 1] = u.y;
+        hc[q].hi[4 * i + 2] = u.z;
+        hc[q].hi[4 * i + 3] = u.w;
+        hc[q].lo[4 * i + 0] = v.x;
+        hc[q].lo[4 * i + 1] = v.y;
+        hc[q].lo[4 * i + 2] = v.z;
+        hc[q].lo[4 * i + 3] = v.w;
+      }
+    }
+    uint32_t code[NIT][2][BITS], smw[NIT][2];
+#pragma unroll
+    for (int q = 0; q < NIT; ++q)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int64_t n = min(n0 + 4 * r + sl, A.H - 1);
+        load_codes<BITS>(code[q][r], blob[q] + A.off_dc + n * rcb + chunk * (4 * BITS));
+        smw[q][r] = *reinterpret_cast<const uint32_t*>(blob[q] + A.off_ds + n * rsb + chunk * 4);
+      }
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sum = dot2(hc[q].hi[i], 0x3F803F80u, sum);
+        sum = dot2(hc[q].lo[i], 0x3F803F80u, sum);
+      }
+      hc[q].sum = sum;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float sc = f16lo(smw[q][r]), mn = f16hi(smw[q][r]);
+        const float mo = mn - 128.0f * sc;
+        part[q][r] = __builtin_fmaf(sc, chunk_dot<BITS, true>(code[q][r], hc[q]), __builtin_fmaf(mo, sum, part[q][r]));
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NIT; ++q) {
+    float v[2] = {part[q][0], part[q][1]};
+    reduce_scatter<2, 1, 3, 0>(v, lane);  // lanes with bit 3 clear hold row step 0, set: row step 1
+    if ((gl & 7) == 0 && pp[q] >= 0) {
+      const int r = gl >> 3, n = n0 + 4 * r + sl;
+      if (n < A.H) {
+        const float val = res[q] ? v[0] : __builtin_nanf("");
+        float yv = val;
+        if constexpr (YBF16) {
+          const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)val);
+          reinterpret_cast<uint16_t*>(A.y)[(int64_t)aa[q] * A.H + n] = b;
+          yv = __uint_as_float((uint32_t)b << 16);
+        } else {
+          reinterpret_cast<float*>(A.y)[(int64_t)aa[q] * A.H + n] = val;
+        }
+        if (ylds) ylds[aa[q] * kRowTile + 4 * r + sl] = yv;
+      }
+    }
+  }
+}
+
+template <int BITS, bool YBF16>
+__global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
+  __shared__ float ylds[kDecodeMaxRows * kRowTile];
+  __shared__ float wl[kDecodeMaxRows];
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * kRowTile;
+  const bool fold = A.out != nullptr;
+  // the combine's inputs, loaded before the routed rows
+  const int ct = threadIdx.x / kRowTile, cr = threadIdx.x % kRowTile;
+  const bool comb = fold && ct < A.T && n0 + cr < A.H;
+  if (fold && (int)threadIdx.x < A.T * A.k) wl[threadIdx.x] = A.w[threadIdx.x];
+  float acc = 0.f;
+  if (comb) {
+    if (A.residual)
+      acc = A.r_bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(A.residual)[(size_t)ct * A.H + n0 + cr]
+                                       << 16)
+                     : reinterpret_cast<const float*>(A.residual)[(size_t)ct * A.H + n0 + cr];
+  }
+  const int nr = *A.nrows;
+  float* yl = fold ? ylds : nullptr;
+  for (int p = wave; p < nr; p += 2 * kRowWaves) {
+    const int p2 = p + kRowWaves;
+    if (p2 < nr) {
+      const int pp[2] = {p, p2};
+      down_rows_items<BITS, 2, YBF16>(A, pp, n0, yl);
+    } else {
+      const int pp[1] = {p};
+      down_rows_items<BITS, 1, YBF16>(A, pp, n0, yl);
+    }
+  }
+  if (!fold) return;
+  __syncthreads();
+  if (comb) {
+    for (int j = 0; j < A.k; ++j) acc = __builtin_fmaf(wl[ct * A.k + j], ylds[(ct * A.k + j) * kRowTile + cr], acc);
+    const size_t o = (size_t)ct * A.H + n0 + cr;
+    A.out[o] = acc;
+    if (A.out_bf16) {
+      uint32_t u = __float_as_uint(acc);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      A.out_bf16[o] = (uint16_t)(u >> 16);
+    }
+  }
+}
+
 // ---- kernels ----------------------------------------------------------------------
 // Gate/up + SwiGLU: one workgroup per (active expert, tile of I).
 template <int BITS, int TM, bool SPLIT, bool WIDE>
@@ -786,8 +940,10 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restr
                                                           const int32_t* __restrict__ sorted_assign,
                                                           const int32_t* __restrict__ active,
                                                           const int32_t* __restrict__ n_active, int k, int max_active,
-                                                          SlotDesc* __restrict__ desc) {
+                                                          SlotDesc* __restrict__ desc, int32_t* __restrict__ rows,
+                                                          int32_t* __restrict__ nrows) {
   const int na = *n_active;
+  if (threadIdx.x == 0) *nrows = na > 0 ? offsets[active[na - 1] + 1] : 0;
   for (int s = threadIdx.x; s < max_active; s += 256) {
     SlotDesc d;
     d.e = s < na ? active[s] : -1;
@@ -801,6 +957,10 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restr
     }
     for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
     desc[s] = d;
+    for (int j = 0; j < d.ne; ++j) {
+      rows[2 * (d.p0 + j)] = d.e;
+      rows[2 * (d.p0 + j) + 1] = sorted_assign[d.p0 + j];
+    }
   }
 }
 
@@ -814,12 +974,11 @@ bool wide_shape(int H, int I) { return H % 2048 == 0 && I % 512 == 0; }
 template <int BITS, bool SPLIT, bool YBF16>
 moe_status launch_wide(DecodeArgs& a, int max_active, hipStream_t s) {
   a.TA = (int)ceil_div(a.I, 4 * kWideNI<SPLIT>);
-  a.TB = (int)ceil_div(a.H, 4 * 4 * kWideRL);
   launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_gateup_kernel<BITS, kWideTM, SPLIT, true>,
            dim3((unsigned)(max_active * a.TA)), dim3(256), 0, s, a);
   if (moe_status st = check_launch("ffn_gateup")) return st;
-  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_kernel<BITS, kWideTM, YBF16, true>, dim3((unsigned)(max_active * a.TB)),
-           dim3(256), 0, s, a);
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
+           dim3(64 * kRowWaves), 0, s, a);
   return check_launch("ffn_down");
 }
 
@@ -876,6 +1035,8 @@ DecodeArgs make_args(const moe_qlayer& q, const void* x, int T, int k, const int
   a.hh = reinterpret_cast<uint16_t*>(W.h);
   a.hl = a.hh + (size_t)T * k * q.I;
   a.y = y;
+  a.rows = W.rows;
+  a.nrows = W.nrows;
   a.ga.G = gcd_pow2_64(q.H / 32);
   a.ga.CPL = (q.H / 32) / a.ga.G;
   a.gb.G = gcd_pow2_64(q.I / 32);
@@ -896,16 +1057,31 @@ DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I) {
   off += up((size_t)n * I * 4);
   W.desc = reinterpret_cast<SlotDesc*>(b + off);
   off += up((size_t)max_active * sizeof(SlotDesc));
+  W.rows = reinterpret_cast<int32_t*>(b + off);
+  off += up((size_t)n * 2 * 4);
+  W.nrows = reinterpret_cast<int32_t*>(b + off);
+  off += 256;
   W.bytes = off;
   return W;
 }
 
 size_t ffn_gemv_ws_bytes(int T, int k, int E, int H, int I) { return decode_ws(nullptr, T, k, E, H, I).bytes; }
 
+bool gemv_folds_combine(int H, int I) { return wide_shape(H, I); }
+
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
-                                 moe_dtype y_t, hipStream_t s) {
+                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s) {
   DecodeArgs a = make_args(q, x, T, k, sorted_assign, n_active, W, y);
+  if (fc.out) {
+    if (!wide_shape(q.H, q.I) || (int64_t)T * k > kDecodeMaxRows || T * kRowTile > 64 * kRowWaves)
+      return fail(MOE_EUNSUPPORTED, "combine cannot be folded for this shape");
+    a.w = fc.w;
+    a.residual = fc.residual;
+    a.r_bf16 = fc.r_t == MOE_BF16;
+    a.out = fc.out;
+    a.out_bf16 = fc.out_bf16;
+  }
   const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
   const bool split = x_t == MOE_F32, yb = y_t == MOE_BF16;
   if (split)
@@ -919,9 +1095,9 @@ moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, in
   const DecodeWs W = decode_ws(ws, T, k, q.E, q.H, q.I);
   const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
   launch_k(MOE_KERNEL_DECODE_PREP, decode_prep_kernel, dim3(1), dim3(256), 0, s, offsets, sorted_assign, active,
-           n_active, k, max_active, W.desc);
+           n_active, k, max_active, W.desc, W.rows, W.nrows);
   if (moe_status st = check_launch("decode_prep")) return st;
-  return launch_ffn_gemv_steps(q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, s);
+  return launch_ffn_gemv_steps(q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, FoldedCombine{}, s);
 }
 
 }  // namespace moe

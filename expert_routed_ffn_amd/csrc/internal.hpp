@@ -50,10 +50,13 @@ struct SlotDesc {
 static_assert(sizeof(SlotDesc) == 128, "SlotDesc is one 128-byte record");
 
 // Decode workspace: h [T*k x I] (fp32, or bf16 hi and lo planes in the same
-// bytes) and the slot descriptors.
+// bytes), the slot descriptors, and per sorted position its (expert,
+// assignment) pair with the number of positions.
 struct DecodeWs {
   float* h;
   SlotDesc* desc;
+  int32_t* rows;   // [T*k][2]
+  int32_t* nrows;  // [1]
   size_t bytes;
 };
 DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I);
@@ -68,9 +71,19 @@ moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, in
 moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                                         int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
                                         int32_t* active, int32_t* n_active, const DecodeWs& W, hipStream_t s);
+// The combine folded into the down kernel when `out` is set (wide shapes only;
+// returns whether it was folded through *folded).
+struct FoldedCombine {
+  const float* w = nullptr;
+  const void* residual = nullptr;
+  moe_dtype r_t = MOE_F32;
+  float* out = nullptr;
+  uint16_t* out_bf16 = nullptr;
+};
+bool gemv_folds_combine(int H, int I);
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
-                                 moe_dtype y_t, hipStream_t s);
+                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);
 
 size_t ffn_mfma_ws_bytes(int T, int k, int E, int H, int I);
 moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,
