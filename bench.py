@@ -143,7 +143,7 @@ def decode_bench(args, torch, moe, synth, oracle):
         "out": torch.empty((T, w.H), dtype=torch.float32, device=dev),
     }
 
-    bufs["dws"] = torch.empty(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8, device=dev)
+    bufs["dws"] = torch.zeros(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8, device=dev)
 
     def step(i, stream=None):
         moe.layer_decode(layers[i % NL], x, lg, k, bufs=bufs, stream=stream)
@@ -377,7 +377,7 @@ def _resident_stack_run(torch, moe, w, big, x_d, lg_d, steps, chunk):
         "dispatch": moe.Dispatch(T, k, E, dev),
         "y": torch.empty((T, k, H), dtype=torch.float32, device=dev),
         "out": torch.empty((T, H), dtype=torch.float32, device=dev),
-        "dws": torch.empty(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8, device=dev),
+        "dws": torch.zeros(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8, device=dev),
     }
     rec = torch.empty((steps, L, T, H), dtype=torch.bfloat16, device=dev)
     out0 = {l: torch.empty((T, H), dtype=torch.float32, device=dev) for l in _check_layers(w)}

@@ -108,133 +108,17 @@ __global__ __launch_bounds__(kBlock) void dispatch_scatter_kernel(const int32_t*
   assign_pos[a] = pos;
 }
 
-// Decode step, part 1 (n = T*k <= kDecodeMaxN assignments): route all T
-// tokens (one wave per token, the same routine as the stand-alone routing
-// kernel), then the same stable grouping as moe_dispatch, done in LDS: the
-// position of assignment a is the number of assignments before it in
-// (expert, index) order; an assignment that is the first of its expert opens
-// an active slot, numbered by the count of such first assignments with a lower
-// expert id.  Every output of moe_dispatch is written, one descriptor per
-// slot (expert, first position, row count, tokens, assignments; e = -1 for
-// slots past n_active) and the (expert, assignment) pair of every sorted
-// position for the FFN kernels.
-constexpr int kDecodeMaxN = kDescT * kMaxK;  // 192
-
-// Counts over the n ids in LDS (padded with kNoId to a multiple of 8), eight
-// ids per step in two 128-bit reads so the reads overlap:
-//   *less += ids < e, *before += (ids == e and index < a), *same += ids == e.
-constexpr int kNoId = 0x7FFFFFFF;
-__device__ __forceinline__ void count_ids(const int32_t* s_id, int n8, int e, int a, int& less, int& before,
-                                          int& same) {
-  less = before = same = 0;
-  for (int b = 0; b < n8; b += 8) {
-    const int4 u = *reinterpret_cast<const int4*>(s_id + b);
-    const int4 v = *reinterpret_cast<const int4*>(s_id + b + 4);
-    const int q[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      less += q[i] < e;
-      same += q[i] == e;
-      before += (q[i] == e) & (b + i < a);
-    }
-  }
-}
-
+// Decode step, part 1: the decode router (routing, grouping, descriptors) in
+// one workgroup.
 template <int EPL>
 __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
     int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc, int max_active,
     int32_t* __restrict__ rows, int32_t* __restrict__ nrows) {
-  __shared__ __align__(16) int32_t s_id[kDecodeMaxN];
-  __shared__ __align__(16) int32_t s_first_e[kDecodeMaxN];  // expert id if the first of its expert, else kNoId
-  __shared__ int32_t s_sorted[kDecodeMaxN];
-  __shared__ int32_t s_slot_e[kDecodeMaxN], s_slot_p0[kDecodeMaxN], s_slot_ne[kDecodeMaxN];
-  __shared__ int32_t s_na;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = T * k, n8 = (n + 7) & ~7;
-  for (int t = wave; t < T; t += kDispWaves) {
-    int id;
-    float wt;
-    dev::route_token<EPL>(logits + (size_t)t * E, E, k, id, wt);
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = id;
-      w[(size_t)t * k + lane] = wt;
-      s_id[t * k + lane] = id;
-    }
-  }
-  if (tid >= n && tid < n8) s_id[tid] = kNoId;
-  __syncthreads();
-  if (tid < n) {
-    const int e = s_id[tid];
-    int less, before, same;
-    count_ids(s_id, n8, e, tid, less, before, same);
-    const int pos = less + before;
-    s_sorted[pos] = tid;
-    sorted_assign[pos] = tid;
-    assign_pos[tid] = pos;
-    s_first_e[tid] = before == 0 ? e : kNoId;
-    if (before == 0) {  // first of its expert: its position opens the expert's rows
-      s_slot_p0[tid] = pos;
-      s_slot_ne[tid] = same;
-    }
-  } else if (tid < n8) {
-    s_first_e[tid] = kNoId;
-  }
-  for (int e = tid; e <= E; e += kBlock) {
-    int less, before, same;
-    count_ids(s_id, n8, e, 0, less, before, same);
-    offsets[e] = less;
-  }
-  __syncthreads();
-  // slot of each first-of-expert assignment = number of first assignments with a lower expert id
-  int slot = -1, p0 = 0, ne = 0, e0 = 0;
-  if (tid < n && s_first_e[tid] != kNoId) {
-    e0 = s_first_e[tid];
-    int less, before, same;
-    count_ids(s_first_e, n8, e0, 0, less, before, same);
-    slot = less;
-    p0 = s_slot_p0[tid];
-    ne = s_slot_ne[tid];
-  }
-  __syncthreads();
-  if (slot >= 0) {
-    s_slot_e[slot] = e0;
-    s_slot_p0[slot] = p0;
-    s_slot_ne[slot] = ne;
-    active[slot] = e0;
-  }
-  if (wave == 0) {
-    int c = 0;
-    for (int b = lane; b < n; b += 64) c += s_first_e[b] != kNoId;
-    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-    if (lane == 0) {
-      s_na = c;
-      *n_active = c;
-    }
-  }
-  __syncthreads();
-  if (tid < n) {
-    const int a = s_sorted[tid];
-    rows[2 * tid] = s_id[a];
-    rows[2 * tid + 1] = a;
-  }
-  if (tid == 0) *nrows = n;
-  const int na = s_na;
-  for (int s2 = tid; s2 < max_active; s2 += kBlock) {
-    SlotDesc d;
-    d.e = s2 < na ? s_slot_e[s2] : -1;
-    d.p0 = s2 < na ? s_slot_p0[s2] : 0;
-    d.ne = s2 < na ? s_slot_ne[s2] : 0;
-    d.pad = 0;
-    for (int j = 0; j < kDescT; ++j) {
-      const int a = j < d.ne ? s_sorted[d.p0 + j] : 0;
-      d.asg[j] = a;
-      d.tok[j] = a / k;
-    }
-    for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
-    desc[s2] = d;
-  }
+  __shared__ dev::RouterLds L;
+  dev::decode_router<EPL, kBlock>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, active, n_active, desc,
+                                  max_active, rows, nrows, L);
 }
 
 __global__ void dispatch_empty_kernel(int E, int32_t* offsets, int32_t* n_active) {
@@ -259,7 +143,7 @@ moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k
                     : epl <= 4 ? route_dispatch_decode_kernel<4>
                     : epl <= 8 ? route_dispatch_decode_kernel<8>
                                : route_dispatch_decode_kernel<16>;
-  if (T * k > kDecodeMaxN) return fail(MOE_EUNSUPPORTED, "route_dispatch_decode: T*k above 192");
+  if (T * k > dev::kDecodeMaxN) return fail(MOE_EUNSUPPORTED, "route_dispatch_decode: T*k above 192");
   launch_k(MOE_KERNEL_ROUTE, kern, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, ids, w, offsets, sorted_assign,
            assign_pos, active, n_active, W.desc, std::min(E, T * k), W.rows, W.nrows);
   return check_launch("route_dispatch_decode");

@@ -26,23 +26,26 @@
 //
 // Two kernel families:
 //  * wide (H a multiple of 2048 and I a multiple of 512, the shapes of the
-//    decode workloads): gate/up rows are split over all 64 lanes of a wave, so
-//    a lane's activation chunk stays in registers for all its rows; down rows
-//    over 16 lanes.  Activation loads are issued before the weight loads, rows
-//    are consumed in load order, and the lane partials of all (row, token)
-//    pairs are reduced together by a reduce-scatter (each exchange level
-//    halves the values a lane carries: permlane32/16 swaps, then DPP), so the
-//    reduction costs about two instructions per value instead of two per
-//    value and level.  The gate/up kernel writes h as separate bf16 hi and lo
-//    planes for the down kernel.
-//  * general (any H, I that are multiples of 32): G = gcd(K/32, 64), a
-//    butterfly reduction per (row, token), h in fp32.
+//    decode workloads).  Gate/up: one workgroup per (active expert, tile of
+//    I); a row is split over all 64 lanes of a wave, so a lane's activation
+//    chunk stays in registers for all its rows; activation loads are issued
+//    before the weight loads and rows are consumed in load order; the lane
+//    partials of all (row, token) pairs are reduced together by a
+//    reduce-scatter (each exchange level halves the values a lane carries:
+//    permlane32/16 swaps, then DPP), about two instructions per value instead
+//    of two per value and level; h is written as separate bf16 hi and lo
+//    planes.  Down: row-tiled, one workgroup per 8 output rows over every
+//    routed row (16 lanes per row), so the layer's combine can be folded into
+//    the same launch (each workgroup owns all contributions to its rows).
+//  * general (any H, I that are multiples of 32): G = gcd(K/32, 64) lanes per
+//    row, a butterfly reduction per (row, token), h in fp32, one workgroup per
+//    (active expert, row tile) for both products.
 //
 // Scheduling.  A decode step moves ~20 MB, a few microseconds of HBM time, so
-// launch and dependency latency dominate.  Every (active expert, row tile) is
-// one workgroup; a per-expert descriptor (id, first row, row count, tokens)
-// built by the preceding single-workgroup kernel lets a workgroup reach its
-// weights and inputs after one dependent load.
+// launch and dependency latency dominate.  A per-expert descriptor (id, first
+// row, row count, tokens) and a per-position (expert, assignment) table built
+// by the preceding single-workgroup kernel let a workgroup reach its weights
+// and inputs after one dependent load.
 #include "internal.hpp"
 
 namespace moe {
@@ -221,6 +224,7 @@ struct DecodeArgs {
   int r_bf16;
   float* out;
   uint16_t* out_bf16;
+  int E;
   int TA, TB;  // gate/up and down workgroups per expert
   Geo ga, gb;
 };
@@ -554,20 +558,15 @@ __device__ __forceinline__ void make_chunk(XChunk<SPLIT>& c, const RawX<SPLIT>& 
   c.sum = s;
 }
 
-// I rows (gate and up) per wave of the wide gate/up kernel; rows per lane of
-// the wide down kernel (each step covers 4 rows, one per 16-lane group).
+// I rows (gate and up) per wave of the wide gate/up kernel.
 #ifndef MOE_WIDE_NI
 #define MOE_WIDE_NI 4
 #endif
 #ifndef MOE_WIDE_NI_SPLIT
 #define MOE_WIDE_NI_SPLIT 2
 #endif
-#ifndef MOE_WIDE_RL
-#define MOE_WIDE_RL 4
-#endif
-constexpr int kWideTM = 3;  // routed rows per pass in the wide kernels
+constexpr int kWideTM = 3;  // routed rows per pass in the wide gate/up kernel
 template <bool SPLIT> constexpr int kWideNI = SPLIT ? MOE_WIDE_NI_SPLIT : MOE_WIDE_NI;
-constexpr int kWideRL = MOE_WIDE_RL;
 
 template <int BITS, int NT, bool SPLIT>
 __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int i0,
@@ -663,107 +662,6 @@ __device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot
     if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT>(A, d, blob, i0, tg);
     else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT>(A, d, blob, i0, tg);
     else gateup_pass_wide<BITS, 1, SPLIT>(A, d, blob, i0, tg);
-    tg += nt;
-  }
-}
-
-template <int BITS, int NT, bool YBF16>
-__device__ __forceinline__ void down_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int n0,
-                                               int rel0, bool resident) {
-  constexpr int RL = kWideRL;
-  const int lane = threadIdx.x & 63, sl = lane >> 4, gl = lane & 15;
-  const int64_t rcb = (int64_t)A.I * BITS / 8, rsb = (int64_t)(A.I / 32) * 4;
-  float part[RL][NT];
-#pragma unroll
-  for (int r = 0; r < RL; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) part[r][t] = 0.f;
-
-  if (resident) {
-    const int cpl = A.I / 512;
-    for (int cc = 0; cc < cpl; ++cc) {
-      const int chunk = gl + 16 * cc;
-      XChunk<true> hc[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const size_t o = (size_t)(d.p0 + rel0 + t) * A.I + 32 * chunk;
-        const uint4* qh = reinterpret_cast<const uint4*>(A.hh + o);
-        const uint4* ql = reinterpret_cast<const uint4*>(A.hl + o);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 a = qh[i], b = ql[i];
-          hc[t].hi[4 * i + 0] = a.x;
-          hc[t].hi[4 * i + 1] = a.y;
-          hc[t].hi[4 * i + 2] = a.z;
-          hc[t].hi[4 * i + 3] = a.w;
-          hc[t].lo[4 * i + 0] = b.x;
-          hc[t].lo[4 * i + 1] = b.y;
-          hc[t].lo[4 * i + 2] = b.z;
-          hc[t].lo[4 * i + 3] = b.w;
-        }
-      }
-      uint32_t code[RL][BITS], smw[RL];
-#pragma unroll
-      for (int r = 0; r < RL; ++r) {
-        const int64_t n = min(n0 + 4 * r + sl, A.H - 1);
-        load_codes<BITS>(code[r], blob + A.off_dc + n * rcb + chunk * (4 * BITS));
-        smw[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_ds + n * rsb + chunk * 4);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s = dot2(hc[t].hi[i], 0x3F803F80u, s);
-          s = dot2(hc[t].lo[i], 0x3F803F80u, s);
-        }
-        hc[t].sum = s;
-      }
-#pragma unroll
-      for (int r = 0; r < RL; ++r) {
-        const float s = f16lo(smw[r]), m = f16hi(smw[r]);
-        const float mo = m - 128.0f * s;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          part[r][t] = __builtin_fmaf(s, chunk_dot<BITS, true>(code[r], hc[t]), __builtin_fmaf(mo, hc[t].sum, part[r][t]));
-      }
-    }
-  }
-
-  constexpr int M = RL * NT, MP = pow2_ceil(M), S = cmin(log2_exact(MP), 4), NVF = MP >> S;
-  float v[MP];
-#pragma unroll
-  for (int m = 0; m < MP; ++m) v[m] = m < M ? part[m / NT][m % NT] : 0.f;
-  reduce_scatter<MP, 1, 3, 0>(v, lane);
-  if ((gl & ((1 << (4 - S)) - 1)) == 0) {
-    const int blk = gl >> (4 - S);
-#pragma unroll
-    for (int q = 0; q < NVF; ++q) {
-      const int m = blk * NVF + q;
-      if (m >= M) continue;
-      const int r = m / NT, t = m % NT, n = n0 + 4 * r + sl;
-      if (n >= A.H) continue;
-      const int64_t a = row_assign(A, d, rel0 + t);
-      const float val = resident ? v[q] : __builtin_nanf("");
-      if constexpr (YBF16) reinterpret_cast<uint16_t*>(A.y)[a * A.H + n] = __builtin_bit_cast(uint16_t, (__bf16)val);
-      else reinterpret_cast<float*>(A.y)[a * A.H + n] = val;
-    }
-  }
-}
-
-template <int BITS, int TM, bool YBF16>
-__device__ __forceinline__ void item_down_wide(const DecodeArgs& A, const Slot& d, int j) {
-  const int wave = threadIdx.x >> 6;
-  const int n0 = (j * 4 + wave) * 4 * kWideRL;
-  if (n0 >= A.H) return;
-  const int idx = resident_index(A, d.e);
-  const bool resident = idx >= 0;
-  const uint8_t* blob = A.base + (int64_t)(resident ? idx : 0) * A.stride;
-  for (int tg = 0; tg < d.ne;) {
-    const int nt = min(d.ne - tg, TM);
-    if (nt >= 3) down_pass_wide<BITS, (TM >= 3 ? 3 : 1), YBF16>(A, d, blob, n0, tg, resident);
-    else if (nt == 2) down_pass_wide<BITS, (TM >= 2 ? 2 : 1), YBF16>(A, d, blob, n0, tg, resident);
-    else down_pass_wide<BITS, 1, YBF16>(A, d, blob, n0, tg, resident);
     tg += nt;
   }
 }
@@ -925,14 +823,13 @@ __global__ __launch_bounds__(256) void ffn_gateup_kernel(DecodeArgs A) {
   else item_gateup<BITS, TM, SPLIT, SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>>(A, d, j);
 }
 
-// Down: one workgroup per (active expert, tile of H).
-template <int BITS, int TM, bool YBF16, bool WIDE>
+// Down (general shapes): one workgroup per (active expert, tile of H).
+template <int BITS, int TM, bool YBF16>
 __global__ __launch_bounds__(256) void ffn_down_kernel(DecodeArgs A) {
   const int s = blockIdx.x / A.TB, j = blockIdx.x % A.TB;
   const Slot d = load_slot(A, s);
   if (d.e < 0) return;  // slot past the active experts
-  if constexpr (WIDE) item_down_wide<BITS, TM, YBF16>(A, d, j);
-  else item_down<BITS, TM, kRLDown<TM>, YBF16>(A, d, j);
+  item_down<BITS, TM, kRLDown<TM>, YBF16>(A, d, j);
 }
 
 // Descriptors from the dispatch arrays (e = -1 for slots past n_active).
@@ -991,7 +888,7 @@ moe_status launch_tm(DecodeArgs& a, int max_active, hipStream_t s) {
   launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_gateup_kernel<BITS, TM, SPLIT, false>, dim3((unsigned)(max_active * a.TA)),
            dim3(256), 0, s, a);
   if (moe_status st = check_launch("ffn_gateup")) return st;
-  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_kernel<BITS, TM, YBF16, false>, dim3((unsigned)(max_active * a.TB)),
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_kernel<BITS, TM, YBF16>, dim3((unsigned)(max_active * a.TB)),
            dim3(256), 0, s, a);
   return check_launch("ffn_down");
 }
@@ -1037,6 +934,7 @@ DecodeArgs make_args(const moe_qlayer& q, const void* x, int T, int k, const int
   a.y = y;
   a.rows = W.rows;
   a.nrows = W.nrows;
+  a.E = q.E;
   a.ga.G = gcd_pow2_64(q.H / 32);
   a.ga.CPL = (q.H / 32) / a.ga.G;
   a.gb.G = gcd_pow2_64(q.I / 32);

@@ -81,6 +81,7 @@ struct FoldedCombine {
   uint16_t* out_bf16 = nullptr;
 };
 bool gemv_folds_combine(int H, int I);
+
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
                                  moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);

@@ -219,5 +219,151 @@ __device__ __forceinline__ void dispatch_block(const int32_t* ids, int n, int E,
   }
 }
 
+
+// ---- decode router: routing, grouping and descriptors in one workgroup -------------
+// For n = T*k <= kDecodeMaxN assignments.  Route all T tokens (one wave per
+// token), then the stable grouping of moe_dispatch done in LDS: the position
+// of assignment a is the number of assignments before it in (expert, index)
+// order; an assignment that is the first of its expert opens an active slot,
+// numbered by the count of such first assignments with a lower expert id.
+// Writes every output of moe_route_topk and moe_dispatch, one descriptor per
+// slot (expert, first position, row count, tokens, assignments; e = -1 for
+// slots past n_active) and the (expert, assignment) pair of every sorted
+// position.
+constexpr int kDecodeMaxN = kDescT * kMaxK;  // 192
+constexpr int kNoId = 0x7FFFFFFF;
+
+struct RouterLds {
+  __align__(16) int32_t id[kDecodeMaxN];
+  __align__(16) int32_t first_e[kDecodeMaxN];  // expert id if the first of its expert, else kNoId
+  int32_t sorted[kDecodeMaxN];
+  int32_t slot_e[kDecodeMaxN], slot_p0[kDecodeMaxN], slot_ne[kDecodeMaxN];
+  int32_t na;
+};
+
+// Counts over the n ids in LDS (padded with kNoId to a multiple of 8), eight
+// ids per step in two 128-bit reads so the reads overlap:
+//   less += ids < e, before += (ids == e and index < a), same += ids == e.
+__device__ __forceinline__ void count_ids(const int32_t* s_id, int n8, int e, int a, int& less, int& before,
+                                          int& same) {
+  less = before = same = 0;
+  for (int b = 0; b < n8; b += 8) {
+    const int4 u = *reinterpret_cast<const int4*>(s_id + b);
+    const int4 v = *reinterpret_cast<const int4*>(s_id + b + 4);
+    const int q[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      less += q[i] < e;
+      same += q[i] == e;
+      before += (q[i] == e) & (b + i < a);
+    }
+  }
+}
+
+template <int EPL, int NT_BLOCK>
+__device__ __forceinline__ void decode_router(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign,
+                                              int32_t* __restrict__ assign_pos, int32_t* __restrict__ active,
+                                              int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc,
+                                              int max_active, int32_t* __restrict__ rows, int32_t* __restrict__ nrows,
+                                              RouterLds& L) {
+  constexpr int NW = NT_BLOCK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = T * k, n8 = (n + 7) & ~7;
+  for (int t = wave; t < T; t += NW) {
+    int id;
+    float wt;
+    route_token<EPL>(logits + (size_t)t * E, E, k, id, wt);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = wt;
+      L.id[t * k + lane] = id;
+    }
+  }
+  for (int i = n + tid; i < n8; i += NT_BLOCK) L.id[i] = kNoId;
+  __syncthreads();
+  for (int a = tid; a < n8; a += NT_BLOCK) {
+    if (a < n) {
+      const int e = L.id[a];
+      int less, before, same;
+      count_ids(L.id, n8, e, a, less, before, same);
+      const int pos = less + before;
+      L.sorted[pos] = a;
+      sorted_assign[pos] = a;
+      assign_pos[a] = pos;
+      L.first_e[a] = before == 0 ? e : kNoId;
+      if (before == 0) {  // first of its expert: its position opens the expert's rows
+        L.slot_p0[a] = pos;
+        L.slot_ne[a] = same;
+      }
+    } else {
+      L.first_e[a] = kNoId;
+    }
+  }
+  __syncthreads();
+  // slot of each first-of-expert assignment = number of first assignments with a lower expert id
+  int slot[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK], p0[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK],
+      ne[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK], e0[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK];
+#pragma unroll
+  for (int r = 0; r < (kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK; ++r) {
+    const int a = tid + r * NT_BLOCK;
+    slot[r] = -1;
+    if (a < n && L.first_e[a] != kNoId) {
+      e0[r] = L.first_e[a];
+      int less, before, same;
+      count_ids(L.first_e, n8, e0[r], 0, less, before, same);
+      slot[r] = less;
+      p0[r] = L.slot_p0[a];
+      ne[r] = L.slot_ne[a];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < (kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK; ++r)
+    if (slot[r] >= 0) {
+      L.slot_e[slot[r]] = e0[r];
+      L.slot_p0[slot[r]] = p0[r];
+      L.slot_ne[slot[r]] = ne[r];
+      active[slot[r]] = e0[r];
+    }
+  if (wave == 0) {
+    int c = 0;
+    for (int b = lane; b < n; b += 64) c += L.first_e[b] != kNoId;
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+    if (lane == 0) {
+      L.na = c;
+      *n_active = c;
+    }
+  }
+  __syncthreads();
+  const int na = L.na;
+  for (int s2 = tid; s2 < max_active; s2 += NT_BLOCK) {
+    SlotDesc d;
+    d.e = s2 < na ? L.slot_e[s2] : -1;
+    d.p0 = s2 < na ? L.slot_p0[s2] : 0;
+    d.ne = s2 < na ? L.slot_ne[s2] : 0;
+    d.pad = 0;
+    for (int j = 0; j < kDescT; ++j) {
+      const int a = j < d.ne ? L.sorted[d.p0 + j] : 0;
+      d.asg[j] = a;
+      d.tok[j] = a / k;
+    }
+    for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
+    desc[s2] = d;
+  }
+  for (int p = tid; p < n; p += NT_BLOCK) {
+    const int a = L.sorted[p];
+    rows[2 * p] = L.id[a];
+    rows[2 * p + 1] = a;
+  }
+  if (tid == 0) *nrows = n;
+  for (int e = tid; e <= E; e += NT_BLOCK) {
+    int less, before, same;
+    count_ids(L.id, n8, e, 0, less, before, same);
+    offsets[e] = less;
+  }
+}
+
 }  // namespace dev
 }  // namespace moe

@@ -331,7 +331,7 @@ def test_layer_decode_repeated_calls_reuse_workspace(moe):
     ex = routed_experts(w, lg)
     layer = moe.ExpertLayer(w.E, w.H, w.I, w.bits, to_dev(ex))
     xd, ld = to_dev_x(w.x()), to_dev(lg)
-    bufs = {"dws": torch.empty(moe.decode_workspace_bytes(layer, w.T, w.k), dtype=torch.uint8, device="cuda")}
+    bufs = {"dws": torch.zeros(moe.decode_workspace_bytes(layer, w.T, w.k), dtype=torch.uint8, device="cuda")}
     outs = []
     for _ in range(3):
         outs.append(to_host(moe.layer_decode(layer, xd, ld, w.k, bufs=bufs)[4]).copy())
