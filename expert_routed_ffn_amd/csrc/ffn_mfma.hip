@@ -21,11 +21,13 @@
 // weights alone already moves outputs by 4e-3 to 9e-3 of their row maximum.
 // Both types run at the same MFMA rate on gfx950.
 //
-// Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x 128 output tile;
-// each wave owns (BM/2) x 64 = (BM/32) x 4 fragments of 16 x 16.  K-steps of
-// 32 go through double-buffered LDS tiles with a 80-byte row pitch (16 lanes
-// reading 16 rows at one column offset hit distinct banks) and one barrier per
-// step.  For gate/up the 128 tile columns are 8 groups of 16: columns 0-7 of a
+// Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile
+// (128 x 128); each wave owns (BM/2) x (BN/2) = (BM/32) x (BN/32) fragments
+// of 16 x 16.  K-steps of 32 go through double-buffered LDS tiles (64-byte
+// rows, 16-byte chunks permuted by row) with one barrier per step; global
+// loads run kPrefetch steps ahead.  Workgroups are ordered so that the N-tiles
+// of one M-tile run on the same die and share its L2 copy of the gathered
+// activation rows.  For gate/up the 128 tile columns are 8 groups of 16: columns 0-7 of a
 // group are gate rows i0+8g .. i0+8g+7 and columns 8-15 the up rows of the same
 // i, so in the MFMA output layout (lane = column) gate and up of one i sit in
 // lanes l and l^8 and SwiGLU needs one lane swap.
@@ -47,9 +49,25 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBN = 128;
 constexpr int kBK = 32;
-constexpr int kPitch = 40;  // fp16 elements per LDS row (80 bytes)
+constexpr int kXcd = 8;  // accelerator dies (each with its own L2) that workgroups are spread over
+#ifndef MOE_MFMA_PREFETCH
+#define MOE_MFMA_PREFETCH 1
+#endif
+constexpr int kPrefetch = MOE_MFMA_PREFETCH;  // K-steps of global loads in flight ahead of the MFMAs
+// LDS tile rows: 0 = 80-byte pitch (padded); 1, 2 = 64-byte pitch with the
+// four 16-byte chunks of a row permuted by chunk ^ ((row >> SHIFT) & 3),
+// SHIFT = 2 or 1.  Layout 1 has a quarter fewer bank-conflict cycles than
+// the padded one on the prefill workload (same time) and a fifth less LDS.
+#ifndef MOE_LDS_SWZ
+#define MOE_LDS_SWZ 1
+#endif
+constexpr int kPitch = MOE_LDS_SWZ == 0 ? 40 : 32;  // fp16 elements per LDS row
+__device__ __forceinline__ int lds_off(int row, int chunk) {  // fp16 offset of 16-byte chunk `chunk` of `row`
+  if constexpr (MOE_LDS_SWZ == 0) return row * kPitch + chunk * 8;
+  constexpr int SH = MOE_LDS_SWZ == 1 ? 2 : 1;
+  return row * kPitch + ((chunk ^ ((row >> SH) & 3)) * 8);
+}
 constexpr float kF16Max = 65504.0f;
 
 // Two floats -> packed fp16 pair (round to nearest even).
@@ -175,14 +193,22 @@ struct GemmArgs {
   void* out;  // h [n x I] fp16 (gate/up) or y [T*k x H] (down)
 };
 
-template <int BITS, int BM, bool GATEUP, bool YBF16>
+template <int BITS, int BM, int BN, bool GATEUP, bool YBF16>
 __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
+  constexpr int kBN = BN;
   constexpr int FM = BM / 32;  // 16-row fragments per wave
+  constexpr int FN = BN / 32;  // 16-column fragments per wave
   constexpr int A_CHUNKS = BM * 4 / 256;  // 16-byte chunks of the A tile per thread per K-step
+  constexpr int B_HALVES = BN / 128;      // 16-weight half rows of the B tile per thread per K-step
   __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][BM * kPitch];
   __shared__ __attribute__((aligned(16))) _Float16 lds_b[2][kBN * kPitch];
 
-  const int tile_idx = blockIdx.x / A.n_tiles_n, nt = blockIdx.x % A.n_tiles_n;
+  // XCD-aware order: workgroups are handed to the kXcd dies round-robin by
+  // index, so block b runs on die b % kXcd; the N-tiles of one M-tile are
+  // given consecutive blocks on the same die, which then reads the M-tile's
+  // activation rows into its own L2 once for all of them.
+  const int xcd = blockIdx.x % kXcd, j = blockIdx.x / kXcd;
+  const int tile_idx = (j / A.n_tiles_n) * kXcd + xcd, nt = j % A.n_tiles_n;
   if (tile_idx >= *A.tile_count) return;
   const TileInfo ti = A.tiles[tile_idx];
   const int e = A.active[ti.slot];
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
       if (m >= rows) continue;
       if constexpr (GATEUP) {
         const int g = col / 16, j = col % 16;
-        const int i = nt * 64 + 8 * g + j;
+        const int i = nt * (kBN / 2) + 8 * g + j;
         if (j < 8 && i < A.I)
           reinterpret_cast<_Float16*>(A.out)[(size_t)(p_begin + m) * A.I + i] = (_Float16)nan;
       } else {
@@ -236,8 +262,8 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
     }
   }
 
-  // ---- B-tile source: this thread decodes 16 weights of one tile row ---------
-  const int b_r = tid >> 1, b_half = tid & 1;
+  // ---- B-tile source: this thread decodes B_HALVES x 16 weights of one tile row
+  const int b_r = B_HALVES == 2 ? tid : tid >> 1, b_half0 = B_HALVES == 2 ? 0 : (tid & 1);
   bool b_ok;
   const uint8_t* b_codes;
   const uint8_t* b_sm;
@@ -246,7 +272,7 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
     int64_t oc, os;
     if constexpr (GATEUP) {
       const int g = b_r / 16, j = b_r % 16;
-      const int i = nt * 64 + 8 * g + (j & 7);
+      const int i = nt * (kBN / 2) + 8 * g + (j & 7);
       b_ok = i < A.I;
       row = b_ok ? i : 0;
       oc = j < 8 ? A.off_c0 : A.off_c1;
@@ -262,75 +288,102 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
     b_sm = blob + os + row * ((int64_t)(K / 32) * 4);
   }
 
-  uint4 a_reg[A_CHUNKS];
-  uint32_t b_code[BITS / 2 == 1 ? 1 : 2];
-  uint32_t b_smw;
+  // One K-step's global data, held in registers between its load and its LDS store.
+  struct Stage {
+    uint4 a[A_CHUNKS];
+    uint32_t code[B_HALVES][BITS / 2 == 1 ? 1 : 2];
+    uint32_t smw;
+  };
 
-  auto load_stage = [&](int ks) {
+  auto load_stage = [&](Stage& st, int ks) {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
-      a_reg[j] = a_ok[j] ? *reinterpret_cast<const uint4*>(a_row[j] + (int64_t)ks * kBK * 2 + a_col16[j] * 16)
-                         : make_uint4(0, 0, 0, 0);
+      st.a[j] = a_ok[j] ? *reinterpret_cast<const uint4*>(a_row[j] + (int64_t)ks * kBK * 2 + a_col16[j] * 16)
+                        : make_uint4(0, 0, 0, 0);
     }
     if (b_ok) {
-      if constexpr (BITS == 2) {
-        b_code[0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 8 + b_half * 4);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(b_codes + (int64_t)ks * 16 + b_half * 8);
-        b_code[0] = v.x;
-        b_code[1] = v.y;
+#pragma unroll
+      for (int hh = 0; hh < B_HALVES; ++hh) {
+        const int b_half = b_half0 + hh;
+        if constexpr (BITS == 2) {
+          st.code[hh][0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 8 + b_half * 4);
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(b_codes + (int64_t)ks * 16 + b_half * 8);
+          st.code[hh][0] = v.x;
+          st.code[hh][1] = v.y;
+        }
       }
-      b_smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
+      st.smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
     }
   };
 
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
       const int c = tid + 256 * j;
       const int m = c / 4;
-      *reinterpret_cast<uint4*>(&lds_a[buf][m * kPitch + a_col16[j] * 8]) = a_reg[j];
+      *reinterpret_cast<uint4*>(&lds_a[buf][lds_off(m, a_col16[j])]) = st.a[j];
     }
-    uint32_t w[8];
-    if (b_ok) {
-      if constexpr (BITS == 2) decode16_b2(b_code[0], b_smw, w);
-      else decode16_b4(b_code[0], b_code[1], b_smw, w);
-    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = 0u;
+    for (int hh = 0; hh < B_HALVES; ++hh) {
+      uint32_t w[8];
+      if (b_ok) {
+        if constexpr (BITS == 2) decode16_b2(st.code[hh][0], st.smw, w);
+        else decode16_b4(st.code[hh][0], st.code[hh][1], st.smw, w);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = 0u;
+      }
+      const int c0 = 2 * (b_half0 + hh);
+      *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0)]) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0 + 1)]) = make_uint4(w[4], w[5], w[6], w[7]);
     }
-    uint4* dst = reinterpret_cast<uint4*>(&lds_b[buf][b_r * kPitch + b_half * 16]);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   };
 
-  f32x4_t acc[FM][4];
+  f32x4_t acc[FM][FN];
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int fj = 0; fj < FN; ++fj) acc[fi][fj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  const int frag_r = lane & 15, frag_k = (lane >> 4) * 8;
-  for (int ks = 0; ks < KS; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < KS) load_stage(ks + 1);
-    f16x8_t af[FM], bfr[4];
+  const int frag_r = lane & 15, frag_q = lane >> 4;  // row in the fragment, 16-byte chunk of K
+  auto mma_stage = [&](int cur) {
+    f16x8_t af[FM], bfr[FN];
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi)
-      af[fi] = *reinterpret_cast<const f16x8_t*>(&lds_a[cur][(wm * (BM / 2) + 16 * fi + frag_r) * kPitch + frag_k]);
+      af[fi] = *reinterpret_cast<const f16x8_t*>(&lds_a[cur][lds_off(wm * (BM / 2) + 16 * fi + frag_r, frag_q)]);
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj)
-      bfr[fj] = *reinterpret_cast<const f16x8_t*>(&lds_b[cur][(wn * 64 + 16 * fj + frag_r) * kPitch + frag_k]);
+    for (int fj = 0; fj < FN; ++fj)
+      bfr[fj] = *reinterpret_cast<const f16x8_t*>(&lds_b[cur][lds_off(wn * (BN / 2) + 16 * fj + frag_r, frag_q)]);
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
-      for (int fj = 0; fj < 4; ++fj)
+      for (int fj = 0; fj < FN; ++fj)
         acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fi], bfr[fj], acc[fi][fj], 0, 0, 0);
-    if (ks + 1 < KS) store_stage(cur ^ 1);
-    __syncthreads();
+  };
+
+  // Software pipeline: global loads run DEPTH K-steps ahead of the MFMAs
+  // (stage s sits in st[s % DEPTH] from its load until its LDS store); LDS is
+  // double-buffered, one barrier per K-step.  The loop is unrolled by DEPTH so
+  // the register stages are static and each store waits only for its own loads.
+  constexpr int DEPTH = kPrefetch;
+  Stage st[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < KS) load_stage(st[d], d);
+  store_stage(st[0], 0);
+  __syncthreads();
+  for (int kb = 0; kb < KS; kb += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int ks = kb + d;
+      if (ks < KS) {
+        if (ks + DEPTH < KS) load_stage(st[d], ks + DEPTH);  // st[d] held stage ks, already in LDS
+        mma_stage(ks & 1);
+        if (ks + 1 < KS) store_stage(st[(d + 1) % DEPTH], (ks + 1) & 1);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- epilogue: lane = output column (lane & 15), rows 4*(lane >> 4) + r ----
@@ -338,19 +391,19 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj)
+    for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[fi][fj][r];
         const int m = wm * (BM / 2) + 16 * fi + rbase + r;
         if constexpr (GATEUP) {
           const float u = __shfl_xor(v, 8, 64);
-          const int i = nt * 64 + 8 * (4 * wn + fj) + col;
+          const int i = nt * (kBN / 2) + 8 * (FN * wn + fj) + col;
           if (col < 8 && m < rows && i < A.I)
             reinterpret_cast<_Float16*>(A.out)[(size_t)(p_begin + m) * A.I + i] =
                 (_Float16)sat_f16(v / (1.0f + expf(-v)) * u);
         } else {
-          const int n = nt * kBN + wn * 64 + 16 * fj + col;
+          const int n = nt * kBN + wn * (BN / 2) + 16 * fj + col;
           if (m < rows && n < A.H) {
             const int64_t a = A.sorted_assign[p_begin + m];
             if constexpr (YBF16) reinterpret_cast<__bf16*>(A.out)[a * A.H + n] = (__bf16)v;
@@ -360,7 +413,18 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
       }
 }
 
-constexpr int kBM = 128;
+#ifndef MOE_MFMA_BM
+#define MOE_MFMA_BM 128
+#endif
+#ifndef MOE_MFMA_BN_GU
+#define MOE_MFMA_BN_GU 128
+#endif
+#ifndef MOE_MFMA_BN_DN
+#define MOE_MFMA_BN_DN 128
+#endif
+constexpr int kBM = MOE_MFMA_BM;
+constexpr int kBNGateUp = MOE_MFMA_BN_GU;
+constexpr int kBNDown = MOE_MFMA_BN_DN;
 
 struct MfmaWs {
   _Float16* x16;
@@ -425,20 +489,21 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   a.off_c1 = L.up_codes;
   a.off_s1 = L.up_sm;
   a.a_src = W.x16;
-  a.n_tiles_n = (int)ceil_div(q.I, 64);
+  a.n_tiles_n = (int)ceil_div(q.I, kBNGateUp / 2);
   a.out = W.h;
-  launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, true, false>,
-           dim3((unsigned)(max_tiles * a.n_tiles_n)), dim3(256), 0, s, a);
+  const int tiles_pad = (int)ceil_div(max_tiles, kXcd) * kXcd;  // whole rounds over the dies
+  launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false>,
+           dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
   if (moe_status st = check_launch("mfma_gateup")) return st;
 
   // down: N = H in tiles of 128
   a.off_c0 = L.down_codes;
   a.off_s0 = L.down_sm;
   a.a_src = W.h;
-  a.n_tiles_n = (int)ceil_div(q.H, kBN);
+  a.n_tiles_n = (int)ceil_div(q.H, kBNDown);
   a.out = y;
-  launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, false, YBF16>,
-           dim3((unsigned)(max_tiles * a.n_tiles_n)), dim3(256), 0, s, a);
+  launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16>,
+           dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
   return check_launch("mfma_down");
 }
 
