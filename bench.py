@@ -53,9 +53,9 @@ BF16_PEAK_TFLOPS = 2500.0
 FETCH_SCALE = 262144.0 / 131088.1875
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "gemv_gateup": {"source": "ffn_gemv.hip", "sha": "5163141f79130649", "fetch_kib": 7428.3, "write_kib": 120.0},
-    "mfma_gateup": {"source": "ffn_mfma.hip", "sha": "451ba60e1e9a1b97", "fetch_kib": 1296275.2,
-                    "write_kib": 86762.3},
+    "gemv_gateup": {"source": "ffn_gemv.hip", "sha": "20f32e9bf8599a1c", "fetch_kib": 7487.4, "write_kib": 60.0},
+    "mfma_gateup": {"source": "ffn_mfma.hip", "sha": "0e606573d460d8b0", "fetch_kib": 362404.4,
+                    "write_kib": 93729.4},
 }
 
 
