@@ -8,16 +8,17 @@ bf16 activations N(0, 1), fp32 router logits N(0, 1) plus a Zipf(1.1)
 popularity bias.  All inputs are seeded synthetic data (no trained weights).
 
 A step is one pass of the whole layer: route + dispatch + expert FFN +
-combine, issued as moe_layer_decode (four launches: routing, dispatch and the
-per-expert descriptors in one workgroup, the gate/up GEMV, the down GEMV, the
-combine); the same step as four separate calls is timed beside it.  Step i uses layer copy i mod --copies (independent allocations of
+combine, issued as moe_layer_decode (two launches: the gate/up GEMV, whose
+workgroups route the tokens themselves, then the down GEMV with the combine
+folded in); the same step as four separate calls is timed beside it.  Step i
+uses layer copy i mod --copies (independent allocations of
 the same layer, 48 by default, about 1 GB of touched weights per cycle) so
 that the 256 MB on-package cache cannot serve one step from the previous one;
 this is the 48-layer stack of the 125B-shaped model with identical weights.
 The K timed steps are captured once in a HIP graph and replayed.
 
 The JSON line also carries:
-  roofline      the dominant kernel (the gate/up dequant-GEMV): algorithmic
+  roofline      the dominant kernel (routing + gate/up dequant-GEMV): algorithmic
                 bytes per launch / its mean duration, timed with HIP events attached
                 to that kernel's own launch (moe_profile_next_launch);
   cpu_baseline  the CPU oracle (scalar C, fp64, one thread) on a bounded
@@ -212,7 +213,8 @@ def decode_bench(args, torch, moe, synth, oracle):
     gu_ms = sum(gu) / len(gu)
     dn_ms = sum(dn) / len(dn)
     gu_plane = w.I * w.H * w.bits // 8 + w.I * (w.H // 32) * 4  # one [I x H] matrix: codes + scale/min
-    gu_bytes = U * 2 * gu_plane + T * w.H * 2 + T * k * w.I * 4  # Wg, Wu of the unique experts; x; h written
+    # Wg, Wu of the unique experts; logits (routed inside the same launch); x; h written
+    gu_bytes = U * 2 * gu_plane + T * w.E * 4 + T * w.H * 2 + T * k * w.I * 4
     dn_bytes = U * (eb - 2 * gu_plane) + T * k * w.I * 4 + T * k * w.H * 4 + T * w.H * 4  # Wd; h; y; out
 
     res = {
@@ -228,7 +230,7 @@ def decode_bench(args, torch, moe, synth, oracle):
             "unit": "GB/s",
             "frac": gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": measured_traffic("gemv_gateup"),
-            "kernel": "ffn_gateup_kernel (expert gate/up dequant-GEMV + SwiGLU)",
+            "kernel": "ffn_route_gateup_kernel (routing + expert gate/up dequant-GEMV + SwiGLU)",
             "bytes_per_launch": gu_bytes,
             "mean_us": gu_ms * 1e3,
             "launches": len(gu),

@@ -262,7 +262,7 @@ def layer_forward(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: 
 
 def layer_decode(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: int, residual=None,
                  y_dtype=torch.float32, out_bf16: torch.Tensor | None = None, bufs=None, stream=None):
-    """moe_layer_decode: the whole layer step (three or four launches).  Returns (ids, w, dispatch, y, out)."""
+    """moe_layer_decode: the whole layer step (two launches for the decode shapes, else four).  Returns (ids, w, dispatch, y, out)."""
     _need(x, "x")
     _need(logits, "logits")
     T, H = x.shape

@@ -209,9 +209,6 @@ moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void
   if (ws_bytes < W.bytes)
     return fail(MOE_EWORKSPACE, fmt("moe_layer_decode: workspace %lld bytes, needs %lld", (long long)ws_bytes,
                                     (long long)W.bytes));
-  if (moe_status st = launch_route_dispatch_decode(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
-                                                   active, n_active, W, stream))
-    return st;
   FoldedCombine fc;
   const bool fold = gemv_folds_combine(q->H, q->I);
   if (fold) {
@@ -221,6 +218,12 @@ moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void
     fc.out = out;
     fc.out_bf16 = out_bf16;
   }
+  if (fold && decode_routes_in_gateup(q->H, q->I, T, k))
+    return launch_decode_routed(*q, logits, x, x_t, T, k, ids, w, offsets, sorted_assign, assign_pos, active,
+                                n_active, W, y, y_t, fc, stream);
+  if (moe_status st = launch_route_dispatch_decode(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
+                                                   active, n_active, W, stream))
+    return st;
   if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, fc, stream))
     return st;
   return fold ? MOE_OK : launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);

@@ -117,8 +117,9 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
     int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc, int max_active,
     int32_t* __restrict__ rows, int32_t* __restrict__ nrows) {
   __shared__ dev::RouterLds L;
-  dev::decode_router<EPL, kBlock>(logits, T, E, k, ids, w, offsets, sorted_assign, assign_pos, active, n_active, desc,
-                                  max_active, rows, nrows, L);
+  dev::decode_route_lds<EPL, kBlock>(logits, T, E, k, L);
+  dev::decode_route_write<kBlock>(L, T, E, k, ids, w, offsets, sorted_assign, assign_pos, active, n_active, desc,
+                                  max_active, rows, nrows);
 }
 
 __global__ void dispatch_empty_kernel(int E, int32_t* offsets, int32_t* n_active) {

@@ -42,11 +42,16 @@
 //    (active expert, row tile) for both products.
 //
 // Scheduling.  A decode step moves ~20 MB, a few microseconds of HBM time, so
-// launch and dependency latency dominate.  A per-expert descriptor (id, first
-// row, row count, tokens) and a per-position (expert, assignment) table built
-// by the preceding single-workgroup kernel let a workgroup reach its weights
-// and inputs after one dependent load.
+// launch and dependency latency dominate.  In the layer step (wide shapes) the
+// gate/up workgroups route the tokens themselves from the logits (a few KB
+// every workgroup reads through the L2) instead of waiting for a routing
+// launch; one extra workgroup writes the routing and dispatch outputs,
+// including a per-position (expert, assignment) table the down kernel reads
+// after the launch boundary.  Called on its own, the gate/up kernel reads a
+// per-expert descriptor (id, first row, row count, tokens) built by a small
+// preceding kernel, one dependent load.
 #include "internal.hpp"
+#include "route_dispatch_dev.hpp"
 
 namespace moe {
 namespace {
@@ -235,16 +240,20 @@ struct DecodeArgs {
 struct Slot {
   const SlotDesc* p;
   int e, p0, ne;
+  int tokv;  // wide kernels: lane j < kDescT holds the token of row j
 };
 
 __device__ __forceinline__ Slot load_slot(const DecodeArgs& A, int s) {
   const SlotDesc* p = A.desc + s;
-  return Slot{p, p->e, p->p0, p->ne};
+  return Slot{p, p->e, p->p0, p->ne, 0};
 }
 
 // Token and assignment of the rel-th routed row of a slot.
 __device__ __forceinline__ int row_token(const DecodeArgs& A, const Slot& d, int rel) {
   return rel < kDescT ? d.p->tok[rel] : A.sorted_assign[d.p0 + rel] / A.k;
+}
+__device__ __forceinline__ int row_token_w(const DecodeArgs& A, const Slot& d, int rel) {
+  return rel < kDescT ? __builtin_amdgcn_readlane(d.tokv, rel) : A.sorted_assign[d.p0 + rel] / A.k;
 }
 __device__ __forceinline__ int row_assign(const DecodeArgs& A, const Slot& d, int rel) {
   return rel < kDescT ? d.p->asg[rel] : A.sorted_assign[d.p0 + rel];
@@ -568,15 +577,14 @@ __device__ __forceinline__ void make_chunk(XChunk<SPLIT>& c, const RawX<SPLIT>& 
 constexpr int kWideTM = 3;  // routed rows per pass in the wide gate/up kernel
 template <bool SPLIT> constexpr int kWideNI = SPLIT ? MOE_WIDE_NI_SPLIT : MOE_WIDE_NI;
 
-template <int BITS, int NT, bool SPLIT>
+template <int BITS, int NT, bool SPLIT, int NI>
 __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int i0,
                                                  int rel0) {
-  constexpr int NI = kWideNI<SPLIT>;
   const int lane = threadIdx.x & 63;
   const int64_t rcb = (int64_t)A.H * BITS / 8, rsb = (int64_t)(A.H / 32) * 4;
   int64_t tok[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) tok[t] = row_token(A, d, rel0 + t);
+  for (int t = 0; t < NT; ++t) tok[t] = row_token_w(A, d, rel0 + t);
   int64_t ri[NI];
 #pragma unroll
   for (int r = 0; r < NI; ++r) ri[r] = min(i0 + r, A.I - 1);  // rows past I compute on a valid row, dropped
@@ -640,9 +648,8 @@ __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot
   }
 }
 
-template <int BITS, int TM, bool SPLIT>
+template <int BITS, int TM, bool SPLIT, int NI>
 __device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot& d, int j) {
-  constexpr int NI = kWideNI<SPLIT>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i0 = (j * 4 + wave) * NI;
   if (i0 >= A.I) return;
@@ -659,9 +666,9 @@ __device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot
   const uint8_t* blob = A.base + (int64_t)idx * A.stride;
   for (int tg = 0; tg < d.ne;) {
     const int nt = min(d.ne - tg, TM);
-    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT>(A, d, blob, i0, tg);
-    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT>(A, d, blob, i0, tg);
-    else gateup_pass_wide<BITS, 1, SPLIT>(A, d, blob, i0, tg);
+    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT, NI>(A, d, blob, i0, tg);
+    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT, NI>(A, d, blob, i0, tg);
+    else gateup_pass_wide<BITS, 1, SPLIT, NI>(A, d, blob, i0, tg);
     tg += nt;
   }
 }
@@ -817,9 +824,13 @@ __global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
 template <int BITS, int TM, bool SPLIT, bool WIDE>
 __global__ __launch_bounds__(256) void ffn_gateup_kernel(DecodeArgs A) {
   const int s = blockIdx.x / A.TA, j = blockIdx.x % A.TA;
-  const Slot d = load_slot(A, s);
+  Slot d = load_slot(A, s);
   if (d.e < 0) return;  // slot past the active experts
-  if constexpr (WIDE) item_gateup_wide<BITS, TM, SPLIT>(A, d, j);
+  if constexpr (WIDE) {
+    const int lane = threadIdx.x & 63;
+    d.tokv = lane < kDescT ? d.p->tok[lane] : 0;
+    item_gateup_wide<BITS, TM, SPLIT, kWideNI<SPLIT>>(A, d, j);
+  }
   else item_gateup<BITS, TM, SPLIT, SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>>(A, d, j);
 }
 
@@ -877,6 +888,70 @@ moe_status launch_wide(DecodeArgs& a, int max_active, hipStream_t s) {
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
            dim3(64 * kRowWaves), 0, s, a);
   return check_launch("ffn_down");
+}
+
+// ---- decode step with the routing inside the gate/up launch ----------------------
+// Every workgroup of the gate/up grid routes the T tokens itself (the same
+// device routine as the stand-alone router, so the same bits), finds its
+// active expert in LDS and goes on with its gate/up rows; workgroup 0 also
+// writes the routing and dispatch outputs, which the down kernel reads after
+// the launch boundary.  This replaces a launch and a descriptor load with a
+// read of T*E logits that every workgroup shares through the L2.
+struct RouteOut {
+  const float* logits;
+  int32_t *ids, *offsets, *sorted_assign, *assign_pos, *active, *n_active, *rows, *nrows;
+  float* w;
+};
+
+// I rows per wave of the routed gate/up kernel: twice the stand-alone kernel's,
+// so the grid (and the routing done per workgroup) is half as large and every
+// workgroup is resident at once.
+#ifndef MOE_ROUTED_NI
+#define MOE_ROUTED_NI 8
+#endif
+#ifndef MOE_ROUTED_NI_SPLIT
+#define MOE_ROUTED_NI_SPLIT 4
+#endif
+#ifndef MOE_ROUTED_NI4
+#define MOE_ROUTED_NI4 4
+#endif
+template <int BITS, bool SPLIT>
+constexpr int kRoutedNI = BITS == 4 ? (SPLIT ? 2 : MOE_ROUTED_NI4) : (SPLIT ? MOE_ROUTED_NI_SPLIT : MOE_ROUTED_NI);
+
+// Workgroup 0 writes the routing and dispatch outputs (the down kernel and the
+// caller read them after the launch); every other workgroup routes in LDS,
+// reads its slot per wave and runs its gate/up rows.
+template <int BITS, bool SPLIT, int EPL>
+__global__ __launch_bounds__(256) void ffn_route_gateup_kernel(DecodeArgs A, RouteOut R) {
+  __shared__ dev::RouterLds L;
+  if (blockIdx.x == 0) {
+    dev::decode_route_lds<EPL, 256>(R.logits, A.T, A.E, A.k, L);
+    dev::decode_route_write<256>(L, A.T, A.E, A.k, R.ids, R.w, R.offsets, R.sorted_assign, R.assign_pos, R.active,
+                                 R.n_active, nullptr, 0, R.rows, R.nrows);
+    return;
+  }
+  dev::route_ids_lds<EPL, 256>(R.logits, A.T, A.E, A.k, L);
+  const int b = blockIdx.x - 1, s = b / A.TA, j = b % A.TA;
+  const dev::WaveSlot ws = dev::wave_slot(L, s, A.k);
+  if (ws.e < 0) return;  // slot past the active experts
+  item_gateup_wide<BITS, kWideTM, SPLIT, kRoutedNI<BITS, SPLIT>>(A, Slot{nullptr, ws.e, ws.p0, ws.ne, ws.tokv}, j);
+}
+
+template <int BITS, bool SPLIT, bool YBF16, int EPL>
+moe_status launch_wide_routed(DecodeArgs& a, const RouteOut& r, int max_active, hipStream_t s) {
+  a.TA = (int)ceil_div(a.I, 4 * kRoutedNI<BITS, SPLIT>);
+  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_route_gateup_kernel<BITS, SPLIT, EPL>,
+           dim3((unsigned)(1 + max_active * a.TA)), dim3(256), 0, s, a, r);
+  if (moe_status st = check_launch("ffn_route_gateup")) return st;
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
+           dim3(64 * kRowWaves), 0, s, a);
+  return check_launch("ffn_down");
+}
+
+template <bool SPLIT, bool YBF16, int EPL>
+moe_status launch_routed_b(DecodeArgs& a, const RouteOut& r, int bits, int max_active, hipStream_t s) {
+  return bits == 2 ? launch_wide_routed<2, SPLIT, YBF16, EPL>(a, r, max_active, s)
+                   : launch_wide_routed<4, SPLIT, YBF16, EPL>(a, r, max_active, s);
 }
 
 template <int BITS, int TM, bool SPLIT, bool YBF16>
@@ -985,6 +1060,47 @@ moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x
   if (split)
     return yb ? launch_b<true, true>(a, q.bits, T, max_active, s) : launch_b<true, false>(a, q.bits, T, max_active, s);
   return yb ? launch_b<false, true>(a, q.bits, T, max_active, s) : launch_b<false, false>(a, q.bits, T, max_active, s);
+}
+
+bool decode_routes_in_gateup(int H, int I, int T, int k) {
+  return wide_shape(H, I) && (int64_t)T * k <= dev::kDecodeMaxN && T * kRowTile <= 64 * kRowWaves;
+}
+
+moe_status launch_decode_routed(const moe_qlayer& q, const float* logits, const void* x, moe_dtype x_t, int T, int k,
+                                int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_assign,
+                                int32_t* assign_pos, int32_t* active, int32_t* n_active, const DecodeWs& W, void* y,
+                                moe_dtype y_t, const FoldedCombine& fc, hipStream_t s) {
+  if (!decode_routes_in_gateup(q.H, q.I, T, k) || !fc.out)
+    return fail(MOE_EUNSUPPORTED, "routing cannot be fused into the gate/up launch for this shape");
+  DecodeArgs a = make_args(q, x, T, k, sorted_assign, n_active, W, y);
+  a.w = w;
+  a.residual = fc.residual;
+  a.r_bf16 = fc.r_t == MOE_BF16;
+  a.out = fc.out;
+  a.out_bf16 = fc.out_bf16;
+  RouteOut r;
+  r.logits = logits;
+  r.ids = ids;
+  r.w = w;
+  r.offsets = offsets;
+  r.sorted_assign = sorted_assign;
+  r.assign_pos = assign_pos;
+  r.active = active;
+  r.n_active = n_active;
+  r.rows = W.rows;
+  r.nrows = W.nrows;
+  const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
+  const bool split = x_t == MOE_F32, yb = y_t == MOE_BF16, big = q.E > 512;
+  if (split) {
+    if (yb) return big ? launch_routed_b<true, true, 16>(a, r, q.bits, max_active, s)
+                       : launch_routed_b<true, true, 8>(a, r, q.bits, max_active, s);
+    return big ? launch_routed_b<true, false, 16>(a, r, q.bits, max_active, s)
+               : launch_routed_b<true, false, 8>(a, r, q.bits, max_active, s);
+  }
+  if (yb) return big ? launch_routed_b<false, true, 16>(a, r, q.bits, max_active, s)
+                     : launch_routed_b<false, true, 8>(a, r, q.bits, max_active, s);
+  return big ? launch_routed_b<false, false, 16>(a, r, q.bits, max_active, s)
+             : launch_routed_b<false, false, 8>(a, r, q.bits, max_active, s);
 }
 
 moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,

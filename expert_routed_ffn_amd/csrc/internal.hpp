@@ -82,6 +82,14 @@ struct FoldedCombine {
 };
 bool gemv_folds_combine(int H, int I);
 
+// Decode step in two launches (wide shapes, T*k <= 192): routing inside the
+// gate/up launch, then the down kernel with the combine folded in.
+bool decode_routes_in_gateup(int H, int I, int T, int k);
+moe_status launch_decode_routed(const moe_qlayer& q, const float* logits, const void* x, moe_dtype x_t, int T, int k,
+                                int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_assign,
+                                int32_t* assign_pos, int32_t* active, int32_t* n_active, const DecodeWs& W, void* y,
+                                moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);
+
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
                                  moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);

@@ -54,19 +54,50 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each 16-lane row, in every lane of the row: quad swaps, then the
+// half-row and row mirrors (each pairs a lane with one in the other half).
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  v += dppf<0x140>(v);
   return v;
+}
+
+// Wave-private LDS of route_token: the candidates, then the k selected in order.
+struct TopkLds {
+  __align__(16) uint32_t key[64];
+  __align__(16) int32_t id[64];
+  uint32_t skey[kMaxK];
+  int32_t sid[kMaxK];
+};
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // One token's routing by one wave.  Lane j < k returns the j-th selected id
 // in *id and its weight in *wt; other lanes return id = -1.  Expert e sits in
-// lane e % 64, slot e / 64.  Each round takes the wave maximum of the keys,
-// then the lowest expert id holding it (the smallest slot with a match, then
-// the lowest lane: ballots over the slots), and clears that one key.
+// lane e % 64, slot e / 64; keys are compared as (key descending, id ascending).
+//
+// Threshold first: tau = the k-th largest of the 64 lane maxima (a bitwise
+// search, two bits per step, on ballot counts).  The k lanes whose maximum is
+// at least tau hold k keys >= tau, so every key of the top k is >= tau.  The
+// candidates (keys >= tau, usually little more than k) are compacted into LDS,
+// each ranks itself against all of them, and the first k land in order.  If
+// ties make the candidates more than 64, k rounds of "wave maximum, lowest id
+// holding it, clear it" select instead.  Both give the exact top k.
 template <int EPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int& id, float& wt) {
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int& id, float& wt,
+                                            TopkLds& S) {
   const int lane = threadIdx.x & 63;
   // all loads first (clamped index, no branch around them), then the keys
   float lv[EPL];
@@ -75,34 +106,85 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   uint32_t key[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) key[j] = (lane + 64 * j < E) ? order_key(lv[j]) : 0u;
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int j = 1; j < EPL; ++j) lm = max(lm, key[j]);
+  // Only the top 16 bits are searched: tau (low bits zero) is then at most
+  // the k-th lane maximum, which keeps the superset property; keys within
+  // one step of the 16-bit grid below it only add candidates.
+  uint32_t tau = 0;  // >= 1 << 16 at the end: at least k lanes hold a finite key
+#pragma unroll
+  for (int b = 30; b >= 16; b -= 2) {
+    const uint32_t c1 = tau | (1u << b), c2 = tau | (2u << b), c3 = tau | (3u << b);
+    const int n1 = __popcll(__ballot(lm >= c1)), n2 = __popcll(__ballot(lm >= c2)), n3 = __popcll(__ballot(lm >= c3));
+    tau = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : tau;
+  }
+  uint64_t cm[EPL];
+  int base[EPL], cnt = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    cm[j] = __ballot(key[j] >= tau);
+    base[j] = cnt;
+    cnt += __popcll(cm[j]);
+  }
   uint32_t mine = 0;
   int mine_id = -1;
-  for (int r = 0; r < k; ++r) {
-    uint32_t lm = key[0];
-#pragma unroll
-    for (int j = 1; j < EPL; ++j) lm = max(lm, key[j]);
-    const uint32_t m = wave_max_u32(lm);
-    int jw = 0, lw = 0;
-#pragma unroll
-    for (int j = EPL - 1; j >= 0; --j) {
-      const uint64_t b = __ballot(key[j] == m);
-      if (b) {
-        jw = j;
-        lw = __builtin_ctzll(b);
-      }
-    }
+  if (cnt <= 64) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j)
-      if (j == jw && lane == lw) key[j] = 0u;
-    if (lane == r) {
-      mine = m;
-      mine_id = jw * 64 + lw;
+      if ((cm[j] >> lane) & 1ull) {
+        const int pos = base[j] + lanes_below(cm[j]);
+        S.key[pos] = key[j];
+        S.id[pos] = lane + 64 * j;
+      }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < cnt) {
+      const uint32_t mk = S.key[lane];
+      const int mi = S.id[lane];
+      int rank = 0;
+      for (int c = 0; c < cnt; c += 4) {  // c + 3 <= 63
+        const uint4 ck = *reinterpret_cast<const uint4*>(&S.key[c]);
+        const int4 ci = *reinterpret_cast<const int4*>(&S.id[c]);
+        const uint32_t kk[4] = {ck.x, ck.y, ck.z, ck.w};
+        const int ii[4] = {ci.x, ci.y, ci.z, ci.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          rank += (c + q < cnt) & ((kk[q] > mk) | ((kk[q] == mk) & (ii[q] < mi)));
+      }
+      if (rank < k) {
+        S.skey[rank] = mk;
+        S.sid[rank] = mi;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) {
+      mine = S.skey[lane];
+      mine_id = S.sid[lane];
+    }
+    __builtin_amdgcn_wave_barrier();
+  } else {
+    for (int r = 0; r < k; ++r) {
+      uint32_t bm = key[0];
+#pragma unroll
+      for (int j = 1; j < EPL; ++j) bm = max(bm, key[j]);
+      int jl = EPL - 1;
+#pragma unroll
+      for (int j = EPL - 2; j >= 0; --j) jl = key[j] == bm ? j : jl;
+      const uint32_t m = wave_max_u32(bm);
+      const uint32_t w = wave_min_u32(bm == m ? (uint32_t)(jl * 64 + lane) : 0xFFFFFFFFu);
+      const int clr = lane == (int)(w & 63) ? jl : -1;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) key[j] = clr == j ? 0u : key[j];
+      if (lane == r) {
+        mine = m;
+        mine_id = (int)w;
+      }
     }
   }
   const float lj = key_logit(mine);
-  const float l0 = __shfl(lj, 0, 64);
+  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lj)));
   const float ex = (lane < k) ? expf(lj - l0) : 0.0f;
-  const float den = wave_sum_f32(ex);
+  const float den = row_sum_f32(ex);  // k <= 16: every term sits in lanes 0..15
   id = (lane < k) ? mine_id : -1;
   wt = (lane < k) ? ex / den : 0.0f;
 }
@@ -226,19 +308,25 @@ __device__ __forceinline__ void dispatch_block(const int32_t* ids, int n, int E,
 // of assignment a is the number of assignments before it in (expert, index)
 // order; an assignment that is the first of its expert opens an active slot,
 // numbered by the count of such first assignments with a lower expert id.
-// Writes every output of moe_route_topk and moe_dispatch, one descriptor per
-// slot (expert, first position, row count, tokens, assignments; e = -1 for
-// slots past n_active) and the (expert, assignment) pair of every sorted
-// position.
+// decode_route_lds leaves all of it in LDS; decode_route_write then writes
+// every output of moe_route_topk and moe_dispatch, one descriptor per slot
+// (expert, first position, row count, tokens, assignments; e = -1 for slots
+// past n_active) and the (expert, assignment) pair of every sorted position.
+// The fused decode gate/up kernel runs the first part in every workgroup and
+// the second in one.
 constexpr int kDecodeMaxN = kDescT * kMaxK;  // 192
 constexpr int kNoId = 0x7FFFFFFF;
 
 struct RouterLds {
   __align__(16) int32_t id[kDecodeMaxN];
   __align__(16) int32_t first_e[kDecodeMaxN];  // expert id if the first of its expert, else kNoId
+  float w[kDecodeMaxN];
   int32_t sorted[kDecodeMaxN];
+  int32_t pos[kDecodeMaxN];
   int32_t slot_e[kDecodeMaxN], slot_p0[kDecodeMaxN], slot_ne[kDecodeMaxN];
+  uint32_t bits[kMaxE / 32];  // experts present (route_ids_lds)
   int32_t na;
+  TopkLds tk[kDescT];  // one per routing wave (wave index < T <= kDescT)
 };
 
 // Counts over the n ids in LDS (padded with kNoId to a multiple of 8), eight
@@ -260,25 +348,21 @@ __device__ __forceinline__ void count_ids(const int32_t* s_id, int n8, int e, in
   }
 }
 
+// Routing and grouping into L.  Ends with a barrier: L is complete for every thread.
 template <int EPL, int NT_BLOCK>
-__device__ __forceinline__ void decode_router(const float* __restrict__ logits, int T, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ w,
-                                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign,
-                                              int32_t* __restrict__ assign_pos, int32_t* __restrict__ active,
-                                              int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc,
-                                              int max_active, int32_t* __restrict__ rows, int32_t* __restrict__ nrows,
-                                              RouterLds& L) {
+__device__ __forceinline__ void decode_route_lds(const float* __restrict__ logits, int T, int E, int k,
+                                                 RouterLds& L) {
   constexpr int NW = NT_BLOCK / 64;
+  constexpr int R = (kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = T * k, n8 = (n + 7) & ~7;
   for (int t = wave; t < T; t += NW) {
     int id;
     float wt;
-    route_token<EPL>(logits + (size_t)t * E, E, k, id, wt);
+    route_token<EPL>(logits + (size_t)t * E, E, k, id, wt, L.tk[wave]);
     if (lane < k) {
-      ids[(size_t)t * k + lane] = id;
-      w[(size_t)t * k + lane] = wt;
       L.id[t * k + lane] = id;
+      L.w[t * k + lane] = wt;
     }
   }
   for (int i = n + tid; i < n8; i += NT_BLOCK) L.id[i] = kNoId;
@@ -290,8 +374,7 @@ __device__ __forceinline__ void decode_router(const float* __restrict__ logits, 
       count_ids(L.id, n8, e, a, less, before, same);
       const int pos = less + before;
       L.sorted[pos] = a;
-      sorted_assign[pos] = a;
-      assign_pos[a] = pos;
+      L.pos[a] = pos;
       L.first_e[a] = before == 0 ? e : kNoId;
       if (before == 0) {  // first of its expert: its position opens the expert's rows
         L.slot_p0[a] = pos;
@@ -303,10 +386,9 @@ __device__ __forceinline__ void decode_router(const float* __restrict__ logits, 
   }
   __syncthreads();
   // slot of each first-of-expert assignment = number of first assignments with a lower expert id
-  int slot[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK], p0[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK],
-      ne[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK], e0[(kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK];
+  int slot[R], p0[R], ne[R], e0[R];
 #pragma unroll
-  for (int r = 0; r < (kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int a = tid + r * NT_BLOCK;
     slot[r] = -1;
     if (a < n && L.first_e[a] != kNoId) {
@@ -320,44 +402,153 @@ __device__ __forceinline__ void decode_router(const float* __restrict__ logits, 
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < (kDecodeMaxN + NT_BLOCK - 1) / NT_BLOCK; ++r)
+  for (int r = 0; r < R; ++r)
     if (slot[r] >= 0) {
       L.slot_e[slot[r]] = e0[r];
       L.slot_p0[slot[r]] = p0[r];
       L.slot_ne[slot[r]] = ne[r];
-      active[slot[r]] = e0[r];
     }
   if (wave == 0) {
     int c = 0;
     for (int b = lane; b < n; b += 64) c += L.first_e[b] != kNoId;
     for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-    if (lane == 0) {
-      L.na = c;
-      *n_active = c;
+    if (lane == 0) L.na = c;
+  }
+  __syncthreads();
+}
+
+// Routing only, for workgroups that then read their slot with wave_slot:
+// L.id (padded with kNoId to kDecodeMaxN) and the bitmap of the experts
+// present.  Ends with a barrier.
+template <int EPL, int NT_BLOCK>
+__device__ __forceinline__ void route_ids_lds(const float* __restrict__ logits, int T, int E, int k, RouterLds& L) {
+  constexpr int NW = NT_BLOCK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = T * k;
+  if (tid < kMaxE / 32) L.bits[tid] = 0u;
+  for (int i = n + tid; i < kDecodeMaxN; i += NT_BLOCK) L.id[i] = kNoId;
+  __syncthreads();
+  for (int t = wave; t < T; t += NW) {
+    int id;
+    float wt;
+    route_token<EPL>(logits + (size_t)t * E, E, k, id, wt, L.tk[wave]);
+    if (lane < k) {
+      L.id[t * k + lane] = id;
+      atomicOr(&L.bits[id >> 5], 1u << (id & 31));
     }
   }
   __syncthreads();
-  const int na = L.na;
-  for (int s2 = tid; s2 < max_active; s2 += NT_BLOCK) {
-    SlotDesc d;
-    d.e = s2 < na ? L.slot_e[s2] : -1;
-    d.p0 = s2 < na ? L.slot_p0[s2] : 0;
-    d.ne = s2 < na ? L.slot_ne[s2] : 0;
-    d.pad = 0;
-    for (int j = 0; j < kDescT; ++j) {
-      const int a = j < d.ne ? L.sorted[d.p0 + j] : 0;
-      d.asg[j] = a;
-      d.tok[j] = a / k;
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_shr(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// One active slot as a wave sees it: expert (-1 past the active experts),
+// first sorted position, row count, and in lane j < min(ne, 64) the token of
+// the slot's j-th row.
+struct WaveSlot {
+  int e, p0, ne, tokv;
+};
+
+// Slot s from route_ids_lds's result, computed by each wave on its own (no
+// barrier): the active experts are the set bits of the bitmap in ascending
+// id, so slot s is its s-th set bit (prefix counts over the bitmap words);
+// its first position is the number of assignments to lower ids and its rows
+// are its assignments in ascending index, the order of the stable dispatch.
+__device__ __forceinline__ WaveSlot wave_slot(const RouterLds& L, int s, int k) {
+  static_assert(kMaxE / 32 == 32 && kDecodeMaxN <= 192, "bitmap words fit one half-wave; ids three per lane");
+  const int lane = threadIdx.x & 63;
+  const uint32_t bw = lane < 32 ? L.bits[lane] : 0u;
+  const int c = __popc(bw);
+  int incl = c;  // inclusive prefix over the 32 words: within 16-lane rows, then across
+  incl += dpp_shr<0x111>(incl);
+  incl += dpp_shr<0x112>(incl);
+  incl += dpp_shr<0x114>(incl);
+  incl += dpp_shr<0x118>(incl);
+  const int row0 = __builtin_amdgcn_readlane(incl, 15);
+  if (lane >= 16) incl += row0;
+  const int na = __builtin_amdgcn_readlane(incl, 31);
+  WaveSlot r{-1, 0, 0, 0};
+  if (s >= na) return r;
+  const int ls = __popcll(__ballot(lane < 32 && incl <= s));  // word holding the s-th bit
+  const int rr = s - (__builtin_amdgcn_readlane(incl, ls) - __builtin_amdgcn_readlane(c, ls));
+  const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)bw, ls);
+  const uint32_t below = lane < 32 ? word & ((1u << (lane & 31)) - 1u) : 0u;
+  const bool hit = lane < 32 && ((word >> (lane & 31)) & 1u) && __popc(below) == rr;
+  const int e = 32 * ls + __builtin_ctzll(__ballot(hit));
+  const int i0 = L.id[lane], i1 = L.id[lane + 64], i2 = L.id[lane + 128];
+  uint64_t m0 = __ballot(i0 == e), m1 = __ballot(i1 == e), m2 = __ballot(i2 == e);
+  r.e = e;
+  r.p0 = __popcll(__ballot(i0 < e)) + __popcll(__ballot(i1 < e)) + __popcll(__ballot(i2 < e));
+  r.ne = __popcll(m0) + __popcll(m1) + __popcll(m2);
+  int asg = 0;
+  const int nl = min(r.ne, 64);
+  for (int j = 0; j < nl; ++j) {
+    int a;
+    if (m0) {
+      a = __builtin_ctzll(m0);
+      m0 &= m0 - 1;
+    } else if (m1) {
+      a = 64 + __builtin_ctzll(m1);
+      m1 &= m1 - 1;
+    } else {
+      a = 128 + __builtin_ctzll(m2);
+      m2 &= m2 - 1;
     }
-    for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
-    desc[s2] = d;
+    if (lane == j) asg = a;
+  }
+  r.tokv = asg / k;
+  return r;
+}
+
+// Slot s of L as a descriptor (e = -1 past n_active).
+__device__ __forceinline__ SlotDesc slot_desc(const RouterLds& L, int s, int k) {
+  const int na = L.na;
+  SlotDesc d;
+  d.e = s < na ? L.slot_e[s] : -1;
+  d.p0 = s < na ? L.slot_p0[s] : 0;
+  d.ne = s < na ? L.slot_ne[s] : 0;
+  d.pad = 0;
+  for (int j = 0; j < kDescT; ++j) {
+    const int a = j < d.ne ? L.sorted[d.p0 + j] : 0;
+    d.asg[j] = a;
+    d.tok[j] = a / k;
+  }
+  for (int j = 0; j < 4; ++j) d.pad2[j] = 0;
+  return d;
+}
+
+// Global outputs from a complete L (no barrier inside).
+template <int NT_BLOCK>
+__device__ __forceinline__ void decode_route_write(const RouterLds& L, int T, int E, int k,
+                                                   int32_t* __restrict__ ids, float* __restrict__ w,
+                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign,
+                                                   int32_t* __restrict__ assign_pos, int32_t* __restrict__ active,
+                                                   int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc,
+                                                   int max_active, int32_t* __restrict__ rows,
+                                                   int32_t* __restrict__ nrows) {
+  const int tid = threadIdx.x;
+  const int n = T * k, n8 = (n + 7) & ~7, na = L.na;
+  for (int a = tid; a < n; a += NT_BLOCK) {
+    ids[a] = L.id[a];
+    w[a] = L.w[a];
+    assign_pos[a] = L.pos[a];
   }
   for (int p = tid; p < n; p += NT_BLOCK) {
     const int a = L.sorted[p];
+    sorted_assign[p] = a;
     rows[2 * p] = L.id[a];
     rows[2 * p + 1] = a;
   }
-  if (tid == 0) *nrows = n;
+  for (int s2 = tid; s2 < na; s2 += NT_BLOCK) active[s2] = L.slot_e[s2];
+  if (tid == 0) {
+    *n_active = na;
+    *nrows = n;
+  }
+  if (desc)
+    for (int s2 = tid; s2 < max_active; s2 += NT_BLOCK) desc[s2] = slot_desc(L, s2, k);
   for (int e = tid; e <= E; e += NT_BLOCK) {
     int less, before, same;
     count_ids(L.id, n8, e, 0, less, before, same);

@@ -6,14 +6,13 @@
 // the lower expert id first, -0.0 equals +0.0.  Weights: softmax over the k
 // selected logits.
 //
-// One wave64 per token (the per-token routine is shared with the fused decode
-// step).  Each lane owns E/64 logits (lane-strided, so the row is read with
-// coalesced loads).  A logit becomes a 64-bit key whose order is the ranking
-// order: the high word maps the float to an unsigned integer that sorts like
-// the float (sign-magnitude to offset binary; +0 and -0 share one key), the
-// low word is ~id so that a lower id wins a tie.  Keys are unique, so k rounds
-// of "lane max, then wave max, owner drops it" give the top k exactly, with no
-// floating-point comparisons.
+// One wave64 per token (the per-token routine is shared with the decode-step
+// kernels, so all produce identical bits).  Each lane owns E/64 logits
+// (lane-strided, so the row is read with coalesced loads).  A logit becomes a
+// 32-bit key whose unsigned order is the float order (sign-magnitude to offset
+// binary; +0 and -0 share one key), so the selection is exact integer work: a
+// threshold from the lane maxima narrows the row to a few candidates, which
+// rank themselves in (key descending, id ascending) order.
 #include "route_dispatch_dev.hpp"
 
 namespace moe {
@@ -22,12 +21,13 @@ namespace {
 template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ dev::TopkLds S[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   int id;
   float wt;
-  dev::route_token<EPL>(logits + (size_t)t * E, E, k, id, wt);
+  dev::route_token<EPL>(logits + (size_t)t * E, E, k, id, wt, S[wave]);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;

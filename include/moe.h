@@ -176,10 +176,11 @@ moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int 
  * and section "2. 왜 대단한가" (1)-(3)).  Every output (ids, w, the dispatch
  * arrays, y, out, out_bf16) is bit-identical to moe_route_topk + moe_dispatch +
  * moe_expert_ffn_q(MOE_PATH_GEMV) + moe_combine on the same inputs.
- * Launches: routing, grouping and the per-expert descriptors in one workgroup;
- * the gate/up + SwiGLU kernel; then, when H is a multiple of 2048 and I of
- * 512, the down kernel with the combine folded in (three launches), else the
- * down kernel and the combine (four).
+ * Launches: when H is a multiple of 2048 and I of 512, two: the gate/up +
+ * SwiGLU kernel, each of whose workgroups routes the T tokens itself (one of
+ * them also writes ids, w and the dispatch arrays), then the down kernel with
+ * the combine folded in.  Other shapes take four: routing, grouping and the
+ * per-expert descriptors in one workgroup; gate/up + SwiGLU; down; combine.
  *   logits [T x E] fp32; x [T x H] (MOE_F32 or MOE_BF16); residual NULL or [T x H].
  *   Outputs as in the four calls; ws of moe_layer_decode_workspace_bytes bytes.
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (T > 12 or the limits above), MOE_EWORKSPACE.

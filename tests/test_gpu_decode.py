@@ -314,6 +314,24 @@ def test_layer_decode_shapes(moe, E, k, H, I, T, bits, x_dtype):
     assert row_rel_err(to_host(b[4]), ref["out"]) <= DECODE_TOL
 
 
+@pytest.mark.parametrize("E,k,T,x_dtype", [
+    (1024, 16, 12, "bf16"),  # T*k = 192 routed rows, the most one step takes; 16 logits per lane
+    (600, 16, 12, "f32"),    # E not a multiple of 64
+    (8, 2, 3, "bf16"),       # fewer experts than lanes
+    (512, 10, 1, "bf16"),
+])
+def test_layer_decode_routing_in_gateup_limits(moe, E, k, T, x_dtype):
+    """Wide shapes route inside every gate/up workgroup: the limits of that path."""
+    w = _custom(E, k, 2048, 512, T, 2, x_dtype, zipf=1.1)
+    x, lg = w.x(), w.logits()
+    ex = routed_experts(w, lg)
+    a, b, _, _ = _four_calls_and_fused(moe, w, x, lg, ex)
+    _assert_bit_identical(a, b, w.T * w.k)
+    ref = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits)
+    assert np.array_equal(to_host(b[0]), ref["ids"])
+    assert row_rel_err(to_host(b[4]), ref["out"]) <= DECODE_TOL
+
+
 def test_layer_decode_all_rows_on_two_experts(moe):
     """Every token routes to the same two experts: 12 rows per expert, several passes."""
     w = _custom(8, 2, 256, 128, 12, 2)
