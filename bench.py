@@ -50,27 +50,34 @@ BF16_PEAK_TFLOPS = 2500.0
 # Memory traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two runs), scaled
 # by what the same counters read for a plain 256 MiB device-to-device copy in the same runs (FETCH_SIZE reads
 # 131,088 KiB for it: x1.99975; WRITE_SIZE reads 262,144 KiB: x1.0).  Each entry is valid only for the kernel
-# source it was measured on (first 16 hex digits of its SHA-256); after a change the traffic is reported null.
+# sources it was measured on (first 16 hex digits of their SHA-256); after a change the traffic is reported null.
 FETCH_SCALE = 262144.0 / 131088.1875
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "gemv_gateup": {"source": "ffn_gemv.hip", "sha": "20f32e9bf8599a1c", "fetch_kib": 7487.4, "write_kib": 60.0},
-    "mfma_gateup": {"source": "ffn_mfma.hip", "sha": "0e606573d460d8b0", "fetch_kib": 362404.4,
-                    "write_kib": 93729.4},
+    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "d619ef0351924a89",
+                    "fetch_kib": 7632.3, "write_kib": 62.9},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "0e606573d460d8b0", "fetch_kib": 362679.1,
+                    "write_kib": 93849.3},
 }
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the counter runs, or None if its source has changed since."""
+def _sources_sha(names) -> str:
     import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the counter runs, or None if its sources have changed since."""
     t = TRAFFIC.get(kernel)
-    if t is None:
+    if t is None or _sources_sha(t["sources"]) != t["sha"]:
         return None
-    src = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", t["source"])
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != t["sha"]:
-            return None
     return (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0
+
+
 METRIC = "MoE-layer tokens/s (decode T=1–3, prefill 8192) + % of HBM / MFMA roofline"
 
 
