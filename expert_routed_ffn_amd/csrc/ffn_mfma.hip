@@ -22,15 +22,17 @@
 // Both types run at the same MFMA rate on gfx950.
 //
 // Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile
-// (128 x 128); each wave owns (BM/2) x (BN/2) = (BM/32) x (BN/32) fragments
-// of 16 x 16.  K-steps of 32 go through double-buffered LDS tiles (64-byte
-// rows, 16-byte chunks permuted by row) with one barrier per step; global
-// loads run kPrefetch steps ahead.  Workgroups are ordered so that the N-tiles
-// of one M-tile run on the same die and share its L2 copy of the gathered
-// activation rows.  For gate/up the 128 tile columns are 8 groups of 16: columns 0-7 of a
-// group are gate rows i0+8g .. i0+8g+7 and columns 8-15 the up rows of the same
-// i, so in the MFMA output layout (lane = column) gate and up of one i sit in
-// lanes l and l^8 and SwiGLU needs one lane swap.
+// (128 x 256); each wave owns (BM/2) x (BN/2) = 64 x 128, i.e. 4 x 8 fragments
+// of 16 x 16, so every fragment read from LDS feeds 4 to 8 MFMAs.  K-steps of
+// 32 go through double-buffered LDS tiles (64-byte rows, 16-byte chunks
+// permuted by row) with one barrier per step; global loads run kPrefetch steps
+// ahead, with no branch around them so that the compiler waits for one stage
+// only.  Workgroups are ordered so that the N-tiles of one M-tile run on the
+// same die and share its L2 copy of the gathered activation rows.  For gate/up
+// the 256 tile columns are 16 groups of 16: columns 0-7 of a group are gate
+// rows i0+8g .. i0+8g+7 and columns 8-15 the up rows of the same i, so in the
+// MFMA output layout (lane = column) gate and up of one i sit in lanes l and
+// l^8 and SwiGLU needs one lane swap.
 //
 // 2-bit decode uses a 4-entry fp16 table per (row, block): the packed pair of
 // codes (c_even, c_odd) in the two halfwords becomes a v_perm_b32 byte selector
@@ -52,7 +54,7 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kBK = 32;
 constexpr int kXcd = 8;  // accelerator dies (each with its own L2) that workgroups are spread over
 #ifndef MOE_MFMA_PREFETCH
-#define MOE_MFMA_PREFETCH 1
+#define MOE_MFMA_PREFETCH 2
 #endif
 constexpr int kPrefetch = MOE_MFMA_PREFETCH;  // K-steps of global loads in flight ahead of the MFMAs
 // LDS tile rows: 0 = 80-byte pitch (padded); 1, 2 = 64-byte pitch with the
@@ -69,6 +71,7 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {  // fp16 offset of 
   return row * kPitch + ((chunk ^ ((row >> SH) & 3)) * 8);
 }
 constexpr float kF16Max = 65504.0f;
+
 
 // Two floats -> packed fp16 pair (round to nearest even).
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
@@ -193,8 +196,14 @@ struct GemmArgs {
   void* out;  // h [n x I] fp16 (gate/up) or y [T*k x H] (down)
 };
 
+// Two waves per SIMD (two workgroups per CU): the compiler keeps the 64 x 128
+// accumulator tile of a wave in VGPRs within that budget.
+#ifndef MOE_MFMA_WAVES_PER_EU
+#define MOE_MFMA_WAVES_PER_EU 2
+#endif
 template <int BITS, int BM, int BN, bool GATEUP, bool YBF16>
-__global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU))) void mfma_ffn_kernel(
+    GemmArgs A) {
   constexpr int kBN = BN;
   constexpr int FM = BM / 32;  // 16-row fragments per wave
   constexpr int FN = BN / 32;  // 16-column fragments per wave
@@ -262,31 +271,31 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
     }
   }
 
-  // ---- B-tile source: this thread decodes B_HALVES x 16 weights of one tile row
-  const int b_r = B_HALVES == 2 ? tid : tid >> 1, b_half0 = B_HALVES == 2 ? 0 : (tid & 1);
-  bool b_ok;
-  const uint8_t* b_codes;
-  const uint8_t* b_sm;
-  {
-    int64_t row;
-    int64_t oc, os;
+  // ---- B-tile rows: tile row r -> weight row in its plane (rows past I or H
+  // read row 0; their columns are never stored)
+  const int64_t row_code_bytes = (int64_t)K * BITS / 8, row_sm_bytes = (int64_t)(K / 32) * 4;
+  auto b_src = [&](int r, const uint8_t*& codes, const uint8_t*& sm) {
+    int64_t row, oc, os;
     if constexpr (GATEUP) {
-      const int g = b_r / 16, j = b_r % 16;
-      const int i = nt * (kBN / 2) + 8 * g + (j & 7);
-      b_ok = i < A.I;
-      row = b_ok ? i : 0;
-      oc = j < 8 ? A.off_c0 : A.off_c1;
-      os = j < 8 ? A.off_s0 : A.off_s1;
+      const int g = r / 16, jj = r % 16;
+      const int i = nt * (kBN / 2) + 8 * g + (jj & 7);
+      row = i < A.I ? i : 0;
+      oc = jj < 8 ? A.off_c0 : A.off_c1;
+      os = jj < 8 ? A.off_s0 : A.off_s1;
     } else {
-      const int n = nt * kBN + b_r;
-      b_ok = n < A.H;
-      row = b_ok ? n : 0;
+      const int n = nt * kBN + r;
+      row = n < A.H ? n : 0;
       oc = A.off_c0;
       os = A.off_s0;
     }
-    b_codes = blob + oc + row * ((int64_t)K * BITS / 8);
-    b_sm = blob + os + row * ((int64_t)(K / 32) * 4);
-  }
+    codes = blob + oc + row * row_code_bytes;
+    sm = blob + os + row * row_sm_bytes;
+  };
+  // this thread decodes B_HALVES x 16 weights of tile row b_r per K-step
+  const int b_r = B_HALVES == 2 ? tid : tid >> 1, b_half0 = B_HALVES == 2 ? 0 : (tid & 1);
+  const uint8_t* b_codes;
+  const uint8_t* b_sm;
+  b_src(b_r, b_codes, b_sm);
 
   // One K-step's global data, held in registers between its load and its LDS store.
   struct Stage {
@@ -295,45 +304,40 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
     uint32_t smw;
   };
 
+  // Loads are unconditional (rows past the tile's end read a valid row whose
+  // results are never stored), so every K-step issues the same loads and the
+  // compiler can wait for one stage while later stages stay in flight.
   auto load_stage = [&](Stage& st, int ks) {
 #pragma unroll
-    for (int j = 0; j < A_CHUNKS; ++j) {
-      st.a[j] = a_ok[j] ? *reinterpret_cast<const uint4*>(a_row[j] + (int64_t)ks * kBK * 2 + a_col16[j] * 16)
-                        : make_uint4(0, 0, 0, 0);
-    }
-    if (b_ok) {
+    for (int jj = 0; jj < A_CHUNKS; ++jj)
+      st.a[jj] = *reinterpret_cast<const uint4*>(a_row[jj] + (int64_t)ks * kBK * 2 + a_col16[jj] * 16);
 #pragma unroll
-      for (int hh = 0; hh < B_HALVES; ++hh) {
-        const int b_half = b_half0 + hh;
-        if constexpr (BITS == 2) {
-          st.code[hh][0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 8 + b_half * 4);
-        } else {
-          const uint2 v = *reinterpret_cast<const uint2*>(b_codes + (int64_t)ks * 16 + b_half * 8);
-          st.code[hh][0] = v.x;
-          st.code[hh][1] = v.y;
-        }
+    for (int hh = 0; hh < B_HALVES; ++hh) {
+      const int b_half = b_half0 + hh;
+      if constexpr (BITS == 2) {
+        st.code[hh][0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 8 + b_half * 4);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(b_codes + (int64_t)ks * 16 + b_half * 8);
+        st.code[hh][0] = v.x;
+        st.code[hh][1] = v.y;
       }
-      st.smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
     }
+    st.smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
   };
 
+  // A chunks and decoded B slice of stage `st` into LDS buffer `buf`.
   auto store_stage = [&](const Stage& st, int buf) {
 #pragma unroll
-    for (int j = 0; j < A_CHUNKS; ++j) {
-      const int c = tid + 256 * j;
+    for (int jj = 0; jj < A_CHUNKS; ++jj) {
+      const int c = tid + 256 * jj;
       const int m = c / 4;
-      *reinterpret_cast<uint4*>(&lds_a[buf][lds_off(m, a_col16[j])]) = st.a[j];
+      *reinterpret_cast<uint4*>(&lds_a[buf][lds_off(m, a_col16[jj])]) = a_ok[jj] ? st.a[jj] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int hh = 0; hh < B_HALVES; ++hh) {
-      uint32_t w[8];
-      if (b_ok) {
-        if constexpr (BITS == 2) decode16_b2(st.code[hh][0], st.smw, w);
-        else decode16_b4(st.code[hh][0], st.code[hh][1], st.smw, w);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0u;
-      }
+      uint32_t w[8];  // rows past I (or H) decode a valid row; their columns are never stored
+      if constexpr (BITS == 2) decode16_b2(st.code[hh][0], st.smw, w);
+      else decode16_b4(st.code[hh][0], st.code[hh][1], st.smw, w);
       const int c0 = 2 * (b_half0 + hh);
       *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0)]) = make_uint4(w[0], w[1], w[2], w[3]);
       *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0 + 1)]) = make_uint4(w[4], w[5], w[6], w[7]);
@@ -365,24 +369,23 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
   // Software pipeline: global loads run DEPTH K-steps ahead of the MFMAs
   // (stage s sits in st[s % DEPTH] from its load until its LDS store); LDS is
   // double-buffered, one barrier per K-step.  The loop is unrolled by DEPTH so
-  // the register stages are static and each store waits only for its own loads.
+  // the register stages are static, and it has no branch around a load or a
+  // store: stages past the end reload the last K-step (never used), so every
+  // iteration issues the same loads and a store waits only for its own stage.
   constexpr int DEPTH = kPrefetch;
   Stage st[DEPTH];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < KS) load_stage(st[d], d);
+  for (int d = 0; d < DEPTH; ++d) load_stage(st[d], min(d, KS - 1));
   store_stage(st[0], 0);
   __syncthreads();
   for (int kb = 0; kb < KS; kb += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int ks = kb + d;
-      if (ks < KS) {
-        if (ks + DEPTH < KS) load_stage(st[d], ks + DEPTH);  // st[d] held stage ks, already in LDS
-        mma_stage(ks & 1);
-        if (ks + 1 < KS) store_stage(st[(d + 1) % DEPTH], (ks + 1) & 1);
-        __syncthreads();
-      }
+      load_stage(st[d], min(ks + DEPTH, KS - 1));  // st[d] held stage ks, already in LDS
+      if (ks < KS) mma_stage(ks & 1);
+      store_stage(st[(d + 1) % DEPTH], (ks + 1) & 1);
+      __syncthreads();
     }
   }
 
@@ -417,10 +420,10 @@ __global__ __launch_bounds__(256) void mfma_ffn_kernel(GemmArgs A) {
 #define MOE_MFMA_BM 128
 #endif
 #ifndef MOE_MFMA_BN_GU
-#define MOE_MFMA_BN_GU 128
+#define MOE_MFMA_BN_GU 256
 #endif
 #ifndef MOE_MFMA_BN_DN
-#define MOE_MFMA_BN_DN 128
+#define MOE_MFMA_BN_DN 256
 #endif
 constexpr int kBM = MOE_MFMA_BM;
 constexpr int kBNGateUp = MOE_MFMA_BN_GU;
