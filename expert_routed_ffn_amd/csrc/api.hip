@@ -130,15 +130,19 @@ moe_status moe_dispatch(const int32_t* ids, int T, int k, int E, int32_t* offset
   return launch_dispatch(ids, T * k, E, offsets, sorted_assign, assign_pos, active, n_active, ws, stream);
 }
 
-static moe_ffn_path resolve_path(moe_ffn_path p, int T) {
-  if (p == MOE_PATH_AUTO) return T <= 8 ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+// AUTO: GEMV up to 256 routed rows, MFMA above.  On the 512-expert, top-10,
+// 2048 x 512 layer the two paths cross between T = 24 (GEMV 100 us, MFMA
+// 110 us per layer step) and T = 32 (118 us, 110 us).
+constexpr int64_t kAutoGemvMaxRows = 256;
+static moe_ffn_path resolve_path(moe_ffn_path p, int T, int k) {
+  if (p == MOE_PATH_AUTO) return (int64_t)T * k <= kAutoGemvMaxRows ? MOE_PATH_GEMV : MOE_PATH_MFMA;
   return p;
 }
 
 size_t moe_expert_ffn_workspace_bytes(const moe_qlayer* q, int T, int k, moe_ffn_path path) {
   if (!q || T < 0 || k < 1) return 0;
   const int n = T * k;
-  if (resolve_path(path, T) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(T, k, q->E, q->H, q->I);
+  if (resolve_path(path, T, k) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(T, k, q->E, q->H, q->I);
   return ffn_mfma_ws_bytes(T, k, q->E, q->H, q->I);
 }
 
@@ -164,7 +168,7 @@ moe_status moe_expert_ffn_q(const moe_qlayer* q, const void* x, moe_dtype x_t, i
   if (!aligned(q->base, 256)) return fail(MOE_EINVAL, "moe_expert_ffn_q: base not 256-byte aligned");
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256))
     return fail(MOE_EINVAL, "moe_expert_ffn_q: x or y not 16-byte aligned, or ws not 256-byte aligned");
-  const moe_ffn_path p = resolve_path(path, T);
+  const moe_ffn_path p = resolve_path(path, T, k);
   const size_t need = moe_expert_ffn_workspace_bytes(q, T, k, p);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(MOE_EWORKSPACE, fmt("moe_expert_ffn_q: workspace %lld bytes, needs %lld", (long long)ws_bytes,
