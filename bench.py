@@ -558,6 +558,71 @@ def sweep_bench(args, torch, moe, synth, oracle):
     }
 
 
+def crossover_bench(args, torch, moe, synth, oracle):
+    """Layer step time against T on the decode layer shape: the GEMV and MFMA expert-FFN paths (four calls each)
+    and moe_layer_decode (T <= 12).  Sets where MOE_PATH_AUTO switches from GEMV to MFMA."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    w0 = synth.decode_verify()
+    ex = w0.experts(nthreads=synth.default_threads())
+    eb, E, k, nc = w0.expert_bytes, w0.E, w0.k, 16
+    lb = E * eb
+    big = torch.empty(nc * lb, dtype=torch.uint8, device=dev)
+    big[:lb].copy_(torch.from_numpy(ex.reshape(-1)))
+    for c in range(1, nc):
+        big[c * lb:(c + 1) * lb].copy_(big[:lb])
+    layers = [moe.ExpertLayer(E, w0.H, w0.I, w0.bits, big[c * lb:(c + 1) * lb]) for c in range(nc)]
+    rows = []
+    for T in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 256, 512):
+        w = synth.Workload(f"crossover_T{T}", E=E, k=k, H=w0.H, I=w0.I, T=T, bits=w0.bits, x_dtype="bf16",
+                           zipf_s=1.1)
+        x = torch.from_numpy(w.x().view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        lg = torch.from_numpy(w.logits()).to(dev)
+        row = {"T": T}
+        for mode in ("gemv", "mfma", "decode"):
+            if mode == "decode" and T > 12:
+                continue
+            bufs = {}
+            if mode == "decode":
+                bufs["dws"] = torch.zeros(moe.decode_workspace_bytes(layers[0], T, k), dtype=torch.uint8,
+                                          device=dev)
+
+                def step(i):
+                    moe.layer_decode(layers[i % nc], x, lg, k, bufs=bufs)
+            else:
+                ids, wt, d, y, out = moe.layer_forward(layers[0], x, lg, k, path=mode)
+                bufs.update(ids=ids, w=wt, dispatch=d, y=y, out=out,
+                            ws=torch.empty(max(1, layers[0].workspace_bytes(T, k, mode)), dtype=torch.uint8,
+                                           device=dev))
+
+                def step(i, mode=mode):
+                    moe.layer_forward(layers[i % nc], x, lg, k, path=mode, bufs=bufs)
+            for i in range(2 * nc):
+                step(i)
+            torch.cuda.synchronize()
+            n = 64 if T <= 64 else 16
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                for i in range(n):
+                    step(i)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            row[f"{mode}_us"] = (time.perf_counter() - t0) / n * 1e6
+            del g
+        rows.append(row)
+        print(f"[crossover] {row}", file=sys.stderr, flush=True)
+    return {
+        "metric": "MoE layer step time against T (decode layer shape)",
+        "workload": "512 experts, top-10, hidden 2048, intermediate 512, 2-bit, Zipf(1.1), bf16 x; 16 rotated "
+                    "layer copies, graph-replayed steps",
+        "unit": "us per layer step", "per_T": rows,
+        "data": "synthetic",
+    }
+
+
 def cpu_baseline(args, oracle, data):
     x_np, lg_np, ex, w = data
     n = args.cpu_steps
@@ -581,9 +646,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-bias", type=float, default=1.0, help="scale of the Zipf(1.1) router bias")
-    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep"], default="layer",
+    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep", "crossover"], default="layer",
                     help="layer: the decode/verify layer (+ prefill), the default; stack125b / sweep: decode "
-                         "steps through a 48- or 40-layer stack, printed as their own JSON line")
+                         "steps through a 48- or 40-layer stack; crossover: layer step time against T for the "
+                         "GEMV and MFMA paths; the last three print their own JSON line")
     ap.add_argument("--stack-steps", type=int, default=0, help="steps of a stack run (default 256 / 64)")
     ap.add_argument("--stack-chunk", type=int, default=16, help="steps per captured graph in stack runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -614,7 +680,7 @@ def main():
         del src, dst
 
     if args.workload != "layer":
-        fn = stack125b_bench if args.workload == "stack125b" else sweep_bench
+        fn = {"stack125b": stack125b_bench, "sweep": sweep_bench, "crossover": crossover_bench}[args.workload]
         print(json.dumps({**fn(args, torch, moe, synth, oracle), "n_gpus": 1}), flush=True)
         return
 
