@@ -77,6 +77,12 @@ def _load():
     L.moe_slot_table_stats.argtypes = [vp, ctypes.POINTER(SlotStats)]
     L.moe_slot_table_map_host.restype = st
     L.moe_slot_table_map_host.argtypes = [vp, vp]
+    L.moe_slot_table_device_bytes.restype = sz
+    L.moe_slot_table_device_bytes.argtypes = [i32, i32, i32]
+    L.moe_slot_table_enable_device.restype = st
+    L.moe_slot_table_enable_device.argtypes = [vp, vp, sz, vp]
+    L.moe_slot_table_resolve_device.restype = st
+    L.moe_slot_table_resolve_device.argtypes = [vp, i32, vp, vp, i32, vp]
     L.moe_slot_table_destroy.restype = None
     L.moe_slot_table_destroy.argtypes = [vp]
     L.moe_slot_table_create_host.restype = st
@@ -322,6 +328,17 @@ class SlotTable:
         _check(lib.moe_slot_table_resolve(self.h, layer, _ptr(d.active), _ptr(d.n_active),
                                           _stream(stream, self.slots.device)))
 
+    def enable_device(self, stream=None):
+        """Switch to device mode: the policy runs on the GPU (state in a device buffer this object keeps)."""
+        nb = int(lib.moe_slot_table_device_bytes(self.L, self.E, self.n_slots))
+        self.state = torch.empty(nb, dtype=torch.uint8, device=self.slots.device)
+        _check(lib.moe_slot_table_enable_device(self.h, _ptr(self.state), nb, _stream(stream, self.slots.device)))
+
+    def resolve_device(self, layer: int, d: Dispatch, max_active: int | None = None, stream=None):
+        m = max_active if max_active is not None else min(self.E, d.T * d.k)
+        _check(lib.moe_slot_table_resolve_device(self.h, layer, _ptr(d.active), _ptr(d.n_active), m,
+                                                 _stream(stream, self.slots.device)))
+
     def layer(self, l: int, H: int, I: int, bits: int) -> ExpertLayer:
         return ExpertLayer(self.E, H, I, bits, self.slots, self.expert_bytes, self.slot_map[l * self.E:(l + 1) * self.E])
 
@@ -362,6 +379,11 @@ class HostSlotTable:
         _check(lib.moe_slot_table_create_host(L, E, n_slots, self._cb, None, ctypes.byref(h)))
         self.h = h
         self.L, self.E = L, E
+
+    def preload(self, pairs):
+        import numpy as np
+        arr = np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1))
+        _check(lib.moe_slot_table_preload(self.h, ctypes.c_void_p(arr.ctypes.data), arr.size // 2, None))
 
     def resolve(self, layer: int, active):
         import numpy as np

@@ -17,11 +17,23 @@
 //
 // Copies go straight from the page-locked master copy into the victim slot
 // with hipMemcpyAsync on the caller's stream, so the FFN kernels enqueued after
-// the resolve see them.  The device map is re-uploaded from a page-locked
+// the resolve see them.
+//
+// Device mode (moe_slot_table_enable_device): the same policy runs on the GPU
+// so that a resolve needs no host round trip.  LRU order is kept as a use
+// stamp per slot (a counter that every touch advances, so the least recently
+// used slot is the one with the smallest stamp; stamps are unique).  One
+// workgroup stamps the hits in active order, then gives each miss, in
+// ascending expert id, the slot of smallest stamp; a second kernel copies the
+// missed blobs from the page-locked master copy (read through its device
+// mapping) into their slots.  Both kernels are ordered on the caller's stream
+// and can be captured in a graph.  The device map is re-uploaded from a page-locked
 // mirror; a resolve waits for the stream before touching the mirror, so the
 // previous upload has always completed before the mirror is modified (no
 // staging buffer is reused while a copy from it may be in flight).
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -47,6 +59,15 @@ struct moe_slot_table {
   std::vector<int32_t> prev, next;
   int32_t head = -1, tail = -1;
   moe_slot_stats stats{};
+  // device mode (state in caller memory)
+  bool device_mode = false;
+  const uint8_t* host_dev = nullptr;  // device mapping of `host`
+  int32_t* d_owner = nullptr;         // [n_slots] l*E + e or -1
+  int64_t* d_stamp = nullptr;         // [n_slots] last use
+  int64_t* d_clock = nullptr;         // [1] stamps handed out so far
+  uint64_t* d_stats = nullptr;        // [5] hits, misses, bytes_h2d, resolves, evictions
+  int32_t* d_copies = nullptr;        // [2 * E] (slot, l*E + e) of the last resolve's misses
+  int32_t* d_ncopies = nullptr;       // [1]
 };
 
 namespace {
@@ -147,6 +168,173 @@ moe_status resolve_list(moe_slot_table* t, int layer, const int32_t* act, int n,
   return MOE_OK;
 }
 
+// ---- device mode -------------------------------------------------------------------------
+struct DevLayout {
+  size_t owner, stamp, clock, stats, copies, ncopies, bytes;
+};
+
+DevLayout dev_layout(int E, int n_slots) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  DevLayout d;
+  size_t off = 0;
+  d.owner = off;
+  off += up((size_t)n_slots * 4);
+  d.stamp = off;
+  off += up((size_t)n_slots * 8);
+  d.clock = off;
+  off += 256;
+  d.stats = off;
+  off += 256;
+  d.copies = off;
+  off += up((size_t)E * 8);
+  d.ncopies = off;
+  off += 256;
+  d.bytes = off;
+  return d;
+}
+
+struct DevArgs {
+  int32_t* map;  // [L*E]
+  int32_t* owner;
+  int64_t* stamp;
+  int64_t* clock;
+  uint64_t* stats;
+  int32_t* copies;
+  int32_t* ncopies;
+  int E, n_slots;
+  uint64_t expert_bytes;
+};
+
+constexpr int kResolveThreads = 1024;
+
+// One resolve in one workgroup.  n_active <= max_active <= n_slots (checked
+// on the host when the call is enqueued; a larger device count is clamped).
+__global__ __launch_bounds__(kResolveThreads) void slot_resolve_kernel(DevArgs a, int layer,
+                                                                       const int32_t* __restrict__ active,
+                                                                       const int32_t* __restrict__ n_active,
+                                                                       int max_active) {
+  constexpr int NW = kResolveThreads / 64;
+  __shared__ int s_miss[moe::kMaxE];
+  __shared__ int s_hits[NW], s_misses[NW];
+  __shared__ int64_t s_v[NW];
+  __shared__ int s_i[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(max(*n_active, 0), max_active);
+  const int64_t clock = *a.clock;
+  const int64_t base = (int64_t)layer * a.E;
+  // hits: stamped in active order; misses: listed in active order (ascending id)
+  const bool valid = tid < n;
+  const int e = valid ? active[tid] : 0;
+  const int s = valid ? a.map[base + e] : -1;
+  const bool hit = valid && s >= 0, miss = valid && s < 0;
+  const uint64_t bh = __ballot(hit), bm = __ballot(miss);
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (lane == 0) {
+    s_hits[wave] = __popcll(bh);
+    s_misses[wave] = __popcll(bm);
+  }
+  __syncthreads();
+  int hb = 0, mb = 0, nh = 0, nm = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) {
+      hb += s_hits[w];
+      mb += s_misses[w];
+    }
+    nh += s_hits[w];
+    nm += s_misses[w];
+  }
+  if (hit) a.stamp[s] = clock + 1 + hb + __popcll(bh & below);
+  if (miss) s_miss[mb + __popcll(bm & below)] = e;
+  __syncthreads();
+  uint64_t evictions = 0;
+  for (int j = 0; j < nm; ++j) {  // victim = smallest stamp; the stamps of this resolve are all larger
+    int64_t bv = INT64_MAX;
+    int bi = 0;
+    for (int q = tid; q < a.n_slots; q += kResolveThreads) {
+      const int64_t v = a.stamp[q];
+      if (v < bv) {
+        bv = v;
+        bi = q;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const int64_t ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov < bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      s_v[wave] = bv;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NW; ++w)
+        if (s_v[w] < bv || (s_v[w] == bv && s_i[w] < bi)) {
+          bv = s_v[w];
+          bi = s_i[w];
+        }
+      const int old = a.owner[bi];
+      if (old >= 0) {
+        a.map[old] = -1;
+        ++evictions;
+      }
+      const int idx = (int)(base + s_miss[j]);
+      a.owner[bi] = idx;
+      a.map[idx] = bi;
+      a.stamp[bi] = clock + 1 + nh + j;
+      a.copies[2 * j] = bi;
+      a.copies[2 * j + 1] = idx;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    *a.clock = clock + nh + nm;
+    *a.ncopies = nm;
+    a.stats[0] += (uint64_t)nh;
+    a.stats[1] += (uint64_t)nm;
+    a.stats[2] += (uint64_t)nm * a.expert_bytes;
+    a.stats[3] += 1;
+    a.stats[4] += evictions;
+  }
+}
+
+constexpr int kCopyThreads = 256, kCopyUnroll = 4;
+constexpr int64_t kCopyChunk = (int64_t)kCopyThreads * 16 * kCopyUnroll;  // bytes per workgroup step
+
+// The last resolve's misses: blob l*E + e of the master copy (device mapping
+// of page-locked host memory) into its slot.  Persistent grid over
+// (miss, chunk) work items.
+__global__ __launch_bounds__(kCopyThreads) void slot_copy_kernel(const int32_t* __restrict__ copies,
+                                                                 const int32_t* __restrict__ ncopies,
+                                                                 const uint8_t* __restrict__ host_dev,
+                                                                 uint8_t* __restrict__ slots, int64_t expert_bytes) {
+  const int nc = *ncopies;
+  const int64_t cpb = (expert_bytes + kCopyChunk - 1) / kCopyChunk;
+  const int64_t total = (int64_t)nc * cpb;
+  for (int64_t w = blockIdx.x; w < total; w += gridDim.x) {
+    const int c = (int)(w / cpb);
+    const int64_t ch = w % cpb;
+    const uint8_t* src = host_dev + (int64_t)copies[2 * c + 1] * expert_bytes;
+    uint8_t* dst = slots + (int64_t)copies[2 * c] * expert_bytes;
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t off = ch * kCopyChunk + ((int64_t)u * kCopyThreads + threadIdx.x) * 16;
+      if (off < expert_bytes) v[u] = *reinterpret_cast<const uint4*>(src + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t off = ch * kCopyChunk + ((int64_t)u * kCopyThreads + threadIdx.x) * 16;
+      if (off < expert_bytes) *reinterpret_cast<uint4*>(dst + off) = v[u];
+    }
+  }
+}
+
+constexpr int kCopyGrid = 512;
+
 void free_table(moe_slot_table* t) {
   if (!t) return;
   if (t->map_mirror) (void)hipHostFree(t->map_mirror);
@@ -218,6 +406,7 @@ moe_status moe_slot_table_create_host(int L, int E, int n_slots, moe_copy_fn cop
 
 moe_status moe_slot_table_preload(moe_slot_table* t, const int32_t* layer_expert, int n, hipStream_t stream) {
   if (!t) return fail(MOE_EINVAL, "moe_slot_table_preload: null table");
+  if (t->device_mode) return fail(MOE_EINVAL, "moe_slot_table_preload: the table is in device mode");
   if (n < 0 || (n > 0 && !layer_expert)) return fail(MOE_EINVAL, "moe_slot_table_preload: bad list");
   for (int i = 0; i < n; ++i) {
     const int l = layer_expert[2 * i], e = layer_expert[2 * i + 1];
@@ -245,6 +434,7 @@ moe_status moe_slot_table_preload(moe_slot_table* t, const int32_t* layer_expert
 moe_status moe_slot_table_resolve(moe_slot_table* t, int layer, const int32_t* active, const int32_t* n_active,
                                   hipStream_t stream) {
   if (!t || t->host_only) return fail(MOE_EINVAL, "moe_slot_table_resolve: not a device table");
+  if (t->device_mode) return fail(MOE_EINVAL, "moe_slot_table_resolve: the table is in device mode");
   if (layer < 0 || layer >= t->L) return fail(MOE_EINVAL, "moe_slot_table_resolve: layer out of range");
   if (!active || !n_active) return fail(MOE_EINVAL, "moe_slot_table_resolve: null pointer");
   // 1) how many experts are active (waits for the routing work queued before us)
@@ -277,14 +467,104 @@ moe_status moe_slot_table_resolve_host(moe_slot_table* t, int layer, const int32
 
 moe_status moe_slot_table_stats(const moe_slot_table* t, moe_slot_stats* out) {
   if (!t || !out) return fail(MOE_EINVAL, "moe_slot_table_stats: null pointer");
+  if (t->device_mode) {
+    uint64_t v[5];
+    if (moe_status st = moe::check_hip(hipMemcpy(v, t->d_stats, sizeof(v), hipMemcpyDeviceToHost),
+                                       "moe_slot_table_stats: copy counters"))
+      return st;
+    *out = moe_slot_stats{v[0], v[1], v[2], v[3], v[4]};
+    return MOE_OK;
+  }
   *out = t->stats;
   return MOE_OK;
 }
 
 moe_status moe_slot_table_map_host(const moe_slot_table* t, int32_t* out) {
   if (!t || !out) return fail(MOE_EINVAL, "moe_slot_table_map_host: null pointer");
+  if (t->device_mode)
+    return moe::check_hip(hipMemcpy(out, t->slot_map_dev, t->map.size() * sizeof(int32_t), hipMemcpyDeviceToHost),
+                          "moe_slot_table_map_host: copy map");
   std::memcpy(out, t->map.data(), t->map.size() * sizeof(int32_t));
   return MOE_OK;
+}
+
+size_t moe_slot_table_device_bytes(int L, int E, int n_slots) {
+  if (L < 1 || E < 1 || E > moe::kMaxE || n_slots < 1) return 0;
+  return dev_layout(E, n_slots).bytes;
+}
+
+moe_status moe_slot_table_enable_device(moe_slot_table* t, void* state, size_t state_bytes, hipStream_t stream) {
+  if (!t || t->host_only) return fail(MOE_EINVAL, "moe_slot_table_enable_device: not a device table");
+  if (t->device_mode) return fail(MOE_EINVAL, "moe_slot_table_enable_device: already in device mode");
+  const DevLayout d = dev_layout(t->E, t->n_slots);
+  if (!state || reinterpret_cast<uintptr_t>(state) % 256)
+    return fail(MOE_EINVAL, "moe_slot_table_enable_device: state must be 256-byte aligned device memory");
+  if (state_bytes < d.bytes)
+    return fail(MOE_EWORKSPACE, "moe_slot_table_enable_device: state is " + std::to_string(state_bytes) +
+                                    " bytes, needs " + std::to_string(d.bytes));
+  void* hd = nullptr;
+  if (moe_status st = moe::check_hip(hipHostGetDevicePointer(&hd, const_cast<uint8_t*>(t->host), 0),
+                                     "moe_slot_table_enable_device: device mapping of the master copy"))
+    return st;
+  if (moe_status st = moe::check_hip(hipStreamSynchronize(stream), "moe_slot_table_enable_device: sync")) return st;
+  // the host policy state in device form: stamps in LRU order (head = 0)
+  std::vector<int64_t> stamp(t->n_slots, 0);
+  int64_t clock = 0;
+  for (int q = t->head; q >= 0; q = t->next[q]) stamp[q] = clock++;
+  const uint64_t stats[5] = {t->stats.hits, t->stats.misses, t->stats.bytes_h2d, t->stats.resolves,
+                             t->stats.evictions};
+  uint8_t* b = static_cast<uint8_t*>(state);
+  t->d_owner = reinterpret_cast<int32_t*>(b + d.owner);
+  t->d_stamp = reinterpret_cast<int64_t*>(b + d.stamp);
+  t->d_clock = reinterpret_cast<int64_t*>(b + d.clock);
+  t->d_stats = reinterpret_cast<uint64_t*>(b + d.stats);
+  t->d_copies = reinterpret_cast<int32_t*>(b + d.copies);
+  t->d_ncopies = reinterpret_cast<int32_t*>(b + d.ncopies);
+  const int32_t zero = 0;
+  const char* what = "moe_slot_table_enable_device: upload";
+  if (moe_status st = moe::check_hip(hipMemcpy(t->d_owner, t->owner.data(), sizeof(int32_t) * t->n_slots,
+                                               hipMemcpyHostToDevice), what))
+    return st;
+  if (moe_status st = moe::check_hip(hipMemcpy(t->d_stamp, stamp.data(), sizeof(int64_t) * t->n_slots,
+                                               hipMemcpyHostToDevice), what))
+    return st;
+  if (moe_status st = moe::check_hip(hipMemcpy(t->d_clock, &clock, sizeof(clock), hipMemcpyHostToDevice), what))
+    return st;
+  if (moe_status st = moe::check_hip(hipMemcpy(t->d_stats, stats, sizeof(stats), hipMemcpyHostToDevice), what))
+    return st;
+  if (moe_status st = moe::check_hip(hipMemcpy(t->d_ncopies, &zero, sizeof(zero), hipMemcpyHostToDevice), what))
+    return st;
+  t->host_dev = static_cast<const uint8_t*>(hd);
+  t->device_mode = true;
+  return MOE_OK;
+}
+
+moe_status moe_slot_table_resolve_device(moe_slot_table* t, int layer, const int32_t* active,
+                                         const int32_t* n_active, int max_active, hipStream_t stream) {
+  if (!t || !t->device_mode) return fail(MOE_EINVAL, "moe_slot_table_resolve_device: table not in device mode");
+  if (layer < 0 || layer >= t->L) return fail(MOE_EINVAL, "moe_slot_table_resolve_device: layer out of range");
+  if (!active || !n_active) return fail(MOE_EINVAL, "moe_slot_table_resolve_device: null pointer");
+  if (max_active < 1 || max_active > t->E)
+    return fail(MOE_EINVAL, "moe_slot_table_resolve_device: max_active outside [1, E]");
+  if (max_active > t->n_slots)
+    return fail(MOE_ECAPACITY, "moe_slot_table_resolve_device: up to " + std::to_string(max_active) +
+                                   " active experts, " + std::to_string(t->n_slots) + " slots");
+  DevArgs a;
+  a.map = t->slot_map_dev;
+  a.owner = t->d_owner;
+  a.stamp = t->d_stamp;
+  a.clock = t->d_clock;
+  a.stats = t->d_stats;
+  a.copies = t->d_copies;
+  a.ncopies = t->d_ncopies;
+  a.E = t->E;
+  a.n_slots = t->n_slots;
+  a.expert_bytes = t->expert_bytes;
+  slot_resolve_kernel<<<1, kResolveThreads, 0, stream>>>(a, layer, active, n_active, max_active);
+  if (moe_status st = moe::check_launch("slot_resolve")) return st;
+  slot_copy_kernel<<<kCopyGrid, kCopyThreads, 0, stream>>>(t->d_copies, t->d_ncopies, t->host_dev, t->slots,
+                                                            (int64_t)t->expert_bytes);
+  return moe::check_launch("slot_copy");
 }
 
 void moe_slot_table_destroy(moe_slot_table* t) { free_table(t); }

@@ -242,8 +242,34 @@ moe_status moe_slot_table_resolve(moe_slot_table* t, int layer, const int32_t* a
 
 moe_status moe_slot_table_stats(const moe_slot_table* t, moe_slot_stats* out);
 
-/* Host view of the map: out (host, [L*E]) = slot of each (layer, expert) or -1. */
+/* Host view of the map: out (host, [L*E]) = slot of each (layer, expert) or -1.
+ * In device mode the map is copied from the device with a blocking copy: call
+ * it after the table's stream has finished (likewise moe_slot_table_stats). */
 moe_status moe_slot_table_map_host(const moe_slot_table* t, int32_t* out);
+
+/*
+ * Device mode: the same policy run on the GPU, so that a resolve needs no host
+ * round trip and can be captured in a graph (passage as above: the compute path
+ * branches on the routing result and moves only the missing experts in).
+ * moe_slot_table_enable_device moves the table's current state (after any
+ * preload) into `state`, device memory of moe_slot_table_device_bytes bytes,
+ * 256-byte aligned, owned by the caller and kept alive with the table; it
+ * waits for `stream` and uploads with blocking copies.  From then on only
+ * moe_slot_table_resolve_device may change the table (resolve and preload
+ * return MOE_EINVAL).  host_experts must have a device mapping (page-locked
+ * memory from hipHostMalloc has one).
+ * moe_slot_table_resolve_device enqueues, on `stream`, one kernel that applies
+ * the policy to active[0 .. *n_active) (device arrays, e.g. from moe_dispatch)
+ * and one that copies the missed blobs from host_experts into their slots, so
+ * kernels that follow on `stream` see the updated slots and map.  max_active
+ * bounds *n_active (e.g. min(E, T*k)); MOE_ECAPACITY if max_active > n_slots.
+ * Maps, copies and counters equal those of moe_slot_table_resolve on the same
+ * sequence of active sets.
+ */
+size_t moe_slot_table_device_bytes(int L, int E, int n_slots);
+moe_status moe_slot_table_enable_device(moe_slot_table* t, void* state, size_t state_bytes, hipStream_t stream);
+moe_status moe_slot_table_resolve_device(moe_slot_table* t, int layer, const int32_t* active,
+                                         const int32_t* n_active, int max_active, hipStream_t stream);
 
 void moe_slot_table_destroy(moe_slot_table* t);
 

@@ -135,3 +135,101 @@ def test_slot_table_capacity_error(moe):
         table.resolve(0, d)
     assert ei.value.status == 6  # MOE_ECAPACITY
     table.close()
+
+
+# ---- device mode: the policy on the GPU ------------------------------------------------
+
+def _warm_pairs(w, n_slots):
+    pairs = []
+    for l in range(w.layers):
+        order = np.argsort(-w.bias(l), kind="stable")[: n_slots // (2 * w.layers)]
+        pairs += [(l, int(e)) for e in order]
+    return pairs
+
+
+@pytest.mark.parametrize("n_slots", [64, 24])
+def test_slot_table_device_mode_matches_resident_bit_for_bit(moe, n_slots):
+    import torch
+    w = _stack()
+    eb = w.expert_bytes
+    host = _host_master(w, torch)
+    dev_all = host.to("cuda")
+    resident = [moe.ExpertLayer(w.E, w.H, w.I, w.bits, dev_all, eb, base_offset=l * w.E * eb) for l in range(w.layers)]
+    ref = _run(moe, torch, w, lambda l: resident[l], steps=4)
+    slots = torch.empty(n_slots * eb, dtype=torch.uint8, device="cuda")
+    smap = torch.empty(w.layers * w.E, dtype=torch.int32, device="cuda")
+    table = moe.SlotTable(w.layers, w.E, n_slots, eb, host, slots, smap)
+    table.preload(_warm_pairs(w, n_slots))
+    table.enable_device()
+    got = _run(moe, torch, w, lambda l: table.layer(l, w.H, w.I, w.bits), steps=4,
+               resolve=lambda l, d: table.resolve_device(l, d))
+    st = table.stats()
+    table.close()
+    assert st["misses"] > 0 and st["resolves"] == 4 * w.layers
+    if n_slots < 64:
+        assert st["evictions"] > 0
+    for (ya, oa), (yb, ob) in zip(ref, got):
+        assert np.array_equal(ya, yb) and np.array_equal(oa, ob)
+
+
+def test_slot_table_device_policy_equals_host_policy(moe):
+    """Random active sets through the device table and a host-only table: same map and counters after every
+    resolve, and every occupied slot holds its blob."""
+    import torch
+    w = _stack(L=3, E=40, H=64, I=32)
+    eb, n_slots = w.expert_bytes, 20
+    host = _host_master(w, torch)
+    slots = torch.zeros(n_slots * eb, dtype=torch.uint8, device="cuda")
+    smap = torch.empty(w.layers * w.E, dtype=torch.int32, device="cuda")
+    table = moe.SlotTable(w.layers, w.E, n_slots, eb, host, slots, smap)
+    ref = moe.HostSlotTable(w.layers, w.E, n_slots)
+    pairs = [(0, 3), (1, 7), (2, 1), (0, 5)]
+    table.preload(pairs)
+    ref.preload(pairs)
+    table.enable_device()
+    rng = np.random.default_rng(11)
+    d = moe.Dispatch(1, n_slots, w.E, "cuda")
+    for it in range(60):
+        layer = int(rng.integers(0, w.layers))
+        n = int(rng.integers(0, n_slots + 1))
+        act = np.sort(rng.choice(w.E, size=n, replace=False)).astype(np.int32)
+        d.active[:n] = torch.from_numpy(act).cuda()
+        d.n_active.fill_(n)
+        table.resolve_device(layer, d, max_active=n_slots)
+        ref.resolve(layer, act)
+        torch.cuda.synchronize()
+        assert np.array_equal(table.map_host(), ref.map_host()), it
+        a, b = table.stats(), ref.stats()
+        assert a["bytes_h2d"] == b["bytes_h2d"] // 256 * eb  # the host-only table counts 256 bytes a copy
+        a.pop("bytes_h2d"), b.pop("bytes_h2d")
+        assert a == b, it
+    m = table.map_host()
+    blobs = host.numpy().reshape(w.layers * w.E, eb)
+    sl = slots.cpu().numpy().reshape(n_slots, eb)
+    for idx in np.nonzero(m >= 0)[0]:
+        assert np.array_equal(sl[m[idx]], blobs[idx]), idx
+    table.close()
+    ref.close()
+
+
+def test_slot_table_device_mode_errors(moe):
+    import torch
+    w = _stack(L=1, E=16, H=64, I=32, T=3, k=4)
+    eb = w.expert_bytes
+    host = _host_master(w, torch)
+    slots = torch.empty(4 * eb, dtype=torch.uint8, device="cuda")
+    smap = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    table = moe.SlotTable(1, w.E, 4, eb, host, slots, smap)
+    ids = torch.tensor([[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11]], dtype=torch.int32, device="cuda")
+    d = moe.dispatch(ids, w.E)
+    with pytest.raises(moe.MoeError) as ei:
+        table.resolve_device(0, d)  # not in device mode yet
+    assert ei.value.status == 1  # MOE_EINVAL
+    table.enable_device()
+    with pytest.raises(moe.MoeError) as ei:
+        table.resolve_device(0, d, max_active=12)
+    assert ei.value.status == 6  # MOE_ECAPACITY
+    with pytest.raises(moe.MoeError) as ei:
+        table.resolve(0, d)
+    assert ei.value.status == 1
+    table.close()
