@@ -528,15 +528,13 @@ def stack125b_bench(args, torch, moe, synth, oracle):
     table.preload([(int(i) // E, int(i) % E) for i in hot])
     table.enable_device()
     views = [table.layer(l, H, w.I, w.bits) for l in range(L)]
-    max_active = min(E, T * k)
+    dbufs = {"ids": ids, "w": wt, "dispatch": d, "y": y, "out": out,
+             "dws": torch.zeros(moe.decode_workspace_bytes(views[0], T, k), dtype=torch.uint8, device=dev)}
 
-    def dstep(s):
+    def dstep(s):  # moe_layer_decode_slots: routing + resolve in one workgroup, miss copy, gate/up, down + combine
         for l in range(L):
-            moe.route_topk(lg_d[s, l], k, ids=ids, w=wt)
-            moe.dispatch(ids, E, out=d)
-            table.resolve_device(l, d, max_active=max_active)
-            moe.expert_ffn_q(views[l], x_d[s, l], k, d, y=y, path="gemv", ws=ws)
-            moe.combine(y, wt, residual=x_d[s, l], out=out, out_bf16=rec[s, l])
+            moe.layer_decode_slots(table, l, views[l], x_d[s, l], lg_d[s, l], k, residual=x_d[s, l],
+                                   out_bf16=rec[s, l], bufs=dbufs)
 
     rec.zero_()
     cap = torch.cuda.Stream()
@@ -567,8 +565,9 @@ def stack125b_bench(args, torch, moe, synth, oracle):
                 "hit_rate": hits / max(1, hits + misses), "misses_per_step": misses / steps,
                 "h2d_MB_per_step": h2d / steps / 1e6, "h2d_GBs_effective_share": h2d / steps / sec_d / 1e9,
                 "bit_identical_to_resident": True,
-                "note": "policy and miss copies on the GPU (copy kernel reading the page-locked master copy "
-                        "through its device mapping); steps captured in graphs"}
+                "note": "moe_layer_decode_slots: the policy runs in the routing workgroup and the misses are "
+                        "copied by a kernel reading the page-locked master copy through its device mapping; no host "
+                        "round trip, steps captured in graphs"}
     print(f"[stack125b] slots, device policy: {sec_d * 1e6:.1f} us/step", file=sys.stderr, flush=True)
     return {
         "metric": "MoE stack tokens/s (125B-shaped stack, decode T=3)",

@@ -94,6 +94,9 @@ def _load():
     L.moe_layer_decode.restype = st
     L.moe_layer_decode.argtypes = [ctypes.POINTER(QLayer), vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                    vp, i32, vp, vp, vp, sz, vp]
+    L.moe_layer_decode_slots.restype = st
+    L.moe_layer_decode_slots.argtypes = [ctypes.POINTER(QLayer), vp, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     L.moe_profile_next_launch.restype = st
     L.moe_profile_next_launch.argtypes = [i32, vp, vp]
     return L
@@ -296,6 +299,40 @@ def layer_decode(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: i
                                 r_t, _ptr(ids), _ptr(w), _ptr(d.offsets), _ptr(d.sorted_assign), _ptr(d.assign_pos),
                                 _ptr(d.active), _ptr(d.n_active), _ptr(y), _dtype_code(y), _ptr(out), _ptr(out_bf16),
                                 _ptr(ws), ws.numel(), _stream(stream, dev)))
+    return ids, w, d, y, out
+
+
+def layer_decode_slots(table, l: int, layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: int,
+                       residual=None, y_dtype=torch.float32, out_bf16: torch.Tensor | None = None, bufs=None,
+                       stream=None):
+    """moe_layer_decode_slots: the layer step through `table` (device mode); `layer` is table.layer(l, ...)."""
+    _need(x, "x")
+    _need(logits, "logits")
+    T, H = x.shape
+    dev = x.device
+    b = bufs or {}
+    ids = b.get("ids")
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = b.get("w")
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    d = b.get("dispatch") or Dispatch(T, k, layer.E, dev)
+    y = b.get("y")
+    if y is None:
+        y = torch.empty((T, k, H), dtype=y_dtype, device=dev)
+    out = b.get("out")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = b.get("dws")
+    if ws is None:
+        ws = torch.empty(max(int(lib.moe_layer_decode_workspace_bytes(ctypes.byref(layer.q), T, k)), 1),
+                         dtype=torch.uint8, device=dev)
+    r_t = MOE_F32 if residual is None else _dtype_code(residual)
+    _check(lib.moe_layer_decode_slots(ctypes.byref(layer.q), table.h, l, _ptr(logits), _ptr(x), _dtype_code(x), T, k,
+                                      _ptr(residual), r_t, _ptr(ids), _ptr(w), _ptr(d.offsets), _ptr(d.sorted_assign),
+                                      _ptr(d.assign_pos), _ptr(d.active), _ptr(d.n_active), _ptr(y), _dtype_code(y),
+                                      _ptr(out), _ptr(out_bf16), _ptr(ws), ws.numel(), _stream(stream, dev)))
     return ids, w, d, y, out
 
 

@@ -233,6 +233,57 @@ moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void
   return fold ? MOE_OK : launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
 }
 
+moe_status moe_layer_decode_slots(const moe_qlayer* q, moe_slot_table* t, int layer, const float* logits,
+                                  const void* x, moe_dtype x_t, int T, int k, const void* residual, moe_dtype r_t,
+                                  int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_assign,
+                                  int32_t* assign_pos, int32_t* active, int32_t* n_active, void* y, moe_dtype y_t,
+                                  float* out, uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "moe_layer_decode_slots";
+  if (!q) return fail(MOE_EINVAL, "moe_layer_decode_slots: null moe_qlayer");
+  if (!slot_table_device_mode(t)) return fail(MOE_EINVAL, "moe_layer_decode_slots: the table is not in device mode");
+  const SlotTableView v = slot_table_view(t);
+  if (layer < 0 || layer >= v.L) return fail(MOE_EINVAL, "moe_layer_decode_slots: layer out of range");
+  if (q->E != v.E || q->base != v.slots || (size_t)q->stride != v.expert_bytes || q->slot_map != v.map + (size_t)layer * v.E)
+    return fail(MOE_EINVAL, "moe_layer_decode_slots: q must be the table's view of `layer` (base = slots, stride = "
+                            "expert_bytes, slot_map = map + layer * E)");
+  if (T < 0) return fail(MOE_EINVAL, "moe_layer_decode_slots: T < 0");
+  if (T > kDescT) return fail(MOE_EUNSUPPORTED, fmt("moe_layer_decode_slots: T=%lld above 12", T));
+  if (moe_status st = check_ek(fn, q->E, k)) return st;
+  if (moe_status st = check_shape(fn, q->H, q->I, q->bits)) return st;
+  if ((int64_t)std::min(q->E, T * k) > v.n_slots)
+    return fail(MOE_ECAPACITY, "moe_layer_decode_slots: more routed experts possible than slots");
+  if (x_t != MOE_F32 && x_t != MOE_BF16) return fail(MOE_EINVAL, "moe_layer_decode_slots: x dtype");
+  if (y_t != MOE_F32 && y_t != MOE_BF16) return fail(MOE_EINVAL, "moe_layer_decode_slots: y dtype");
+  if (residual && r_t != MOE_F32 && r_t != MOE_BF16) return fail(MOE_EINVAL, "moe_layer_decode_slots: residual dtype");
+  if (T == 0) return MOE_OK;
+  if (!logits || !x || !ids || !w || !offsets || !sorted_assign || !assign_pos || !active || !n_active || !y || !out)
+    return fail(MOE_EINVAL, "moe_layer_decode_slots: null pointer");
+  const uintptr_t r_align = r_t == MOE_F32 ? 16 : 8;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(out, 16) || !aligned(ws, 256) ||
+      (residual && !aligned(residual, r_align)) || (out_bf16 && !aligned(out_bf16, 8)))
+    return fail(MOE_EINVAL, "moe_layer_decode_slots: misaligned buffer");
+  const DecodeWs W = decode_ws(ws, T, k, q->E, q->H, q->I);
+  if (ws_bytes < W.bytes)
+    return fail(MOE_EWORKSPACE, fmt("moe_layer_decode_slots: workspace %lld bytes, needs %lld", (long long)ws_bytes,
+                                    (long long)W.bytes));
+  if (moe_status st = launch_route_dispatch_resolve(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
+                                                    active, n_active, W, t, layer, stream))
+    return st;
+  if (moe_status st = launch_slot_copy(t, stream)) return st;
+  FoldedCombine fc;
+  const bool fold = gemv_folds_combine(q->H, q->I);
+  if (fold) {
+    fc.w = w;
+    fc.residual = residual;
+    fc.r_t = r_t;
+    fc.out = out;
+    fc.out_bf16 = out_bf16;
+  }
+  if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, fc, stream))
+    return st;
+  return fold ? MOE_OK : launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
+}
+
 moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int k, int H, const void* residual,
                        moe_dtype r_t, float* out, uint16_t* out_bf16, hipStream_t stream) {
   if (T < 0 || H < 1) return fail(MOE_EINVAL, "moe_combine: T < 0 or H < 1");

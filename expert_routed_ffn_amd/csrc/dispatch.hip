@@ -20,6 +20,7 @@
 #include <algorithm>
 
 #include "route_dispatch_dev.hpp"
+#include "slot_dev.hpp"
 
 namespace moe {
 namespace {
@@ -122,6 +123,22 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_decode_kernel(
                                   max_active, rows, nrows);
 }
 
+// Decode router, then the slot table's resolve of the routed experts, in the
+// same workgroup (the active list is still in LDS).
+template <int EPL>
+__global__ __launch_bounds__(kBlock) void route_dispatch_resolve_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotDesc* __restrict__ desc, int max_active,
+    int32_t* __restrict__ rows, int32_t* __restrict__ nrows, SlotDevArgs sa, int layer) {
+  __shared__ dev::RouterLds L;
+  __shared__ dev::SlotLds<kBlock> S;
+  dev::decode_route_lds<EPL, kBlock>(logits, T, E, k, L);
+  dev::decode_route_write<kBlock>(L, T, E, k, ids, w, offsets, sorted_assign, assign_pos, active, n_active, desc,
+                                  max_active, rows, nrows);
+  dev::slot_resolve_block<kBlock>(sa, layer, L.slot_e, L.na, S);
+}
+
 __global__ void dispatch_empty_kernel(int E, int32_t* offsets, int32_t* n_active) {
   for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = 0;
   if (threadIdx.x == 0) *n_active = 0;
@@ -148,6 +165,22 @@ moe_status launch_route_dispatch_decode(const float* logits, int T, int E, int k
   launch_k(MOE_KERNEL_ROUTE, kern, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, ids, w, offsets, sorted_assign,
            assign_pos, active, n_active, W.desc, std::min(E, T * k), W.rows, W.nrows);
   return check_launch("route_dispatch_decode");
+}
+
+moe_status launch_route_dispatch_resolve(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                         int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                                         int32_t* active, int32_t* n_active, const DecodeWs& W,
+                                         const moe_slot_table* t, int layer, hipStream_t s) {
+  const int epl = (int)ceil_div(E, 64);
+  const auto kern = epl <= 1   ? route_dispatch_resolve_kernel<1>
+                    : epl <= 2 ? route_dispatch_resolve_kernel<2>
+                    : epl <= 4 ? route_dispatch_resolve_kernel<4>
+                    : epl <= 8 ? route_dispatch_resolve_kernel<8>
+                               : route_dispatch_resolve_kernel<16>;
+  if (T * k > dev::kDecodeMaxN) return fail(MOE_EUNSUPPORTED, "route_dispatch_resolve: T*k above 192");
+  launch_k(MOE_KERNEL_ROUTE, kern, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, ids, w, offsets, sorted_assign,
+           assign_pos, active, n_active, W.desc, std::min(E, T * k), W.rows, W.nrows, slot_dev_args(t), layer);
+  return check_launch("route_dispatch_resolve");
 }
 
 moe_status launch_dispatch(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* sorted_assign,

@@ -90,6 +90,24 @@ moe_status launch_decode_routed(const moe_qlayer& q, const float* logits, const 
                                 int32_t* assign_pos, int32_t* active, int32_t* n_active, const DecodeWs& W, void* y,
                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);
 
+// Slot table in device mode (slot_table.hip).
+struct SlotDevArgs;
+struct SlotTableView {
+  int L, E, n_slots;
+  size_t expert_bytes;
+  const uint8_t* slots;
+  const int32_t* map;
+};
+bool slot_table_device_mode(const moe_slot_table* t);
+SlotDevArgs slot_dev_args(const moe_slot_table* t);
+SlotTableView slot_table_view(const moe_slot_table* t);
+moe_status launch_slot_copy(const moe_slot_table* t, hipStream_t stream);
+// Decode router followed by the table's resolve of the routed experts, one workgroup (dispatch.hip).
+moe_status launch_route_dispatch_resolve(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                         int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                                         int32_t* active, int32_t* n_active, const DecodeWs& W,
+                                         const moe_slot_table* t, int layer, hipStream_t s);
+
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
                                  moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);

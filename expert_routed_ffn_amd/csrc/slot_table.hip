@@ -39,6 +39,7 @@
 #include <vector>
 
 #include "internal.hpp"
+#include "slot_dev.hpp"
 
 struct moe_slot_table {
   int L = 0, E = 0, n_slots = 0;
@@ -193,112 +194,16 @@ DevLayout dev_layout(int E, int n_slots) {
   return d;
 }
 
-struct DevArgs {
-  int32_t* map;  // [L*E]
-  int32_t* owner;
-  int64_t* stamp;
-  int64_t* clock;
-  uint64_t* stats;
-  int32_t* copies;
-  int32_t* ncopies;
-  int E, n_slots;
-  uint64_t expert_bytes;
-};
-
 constexpr int kResolveThreads = 1024;
 
 // One resolve in one workgroup.  n_active <= max_active <= n_slots (checked
 // on the host when the call is enqueued; a larger device count is clamped).
-__global__ __launch_bounds__(kResolveThreads) void slot_resolve_kernel(DevArgs a, int layer,
+__global__ __launch_bounds__(kResolveThreads) void slot_resolve_kernel(moe::SlotDevArgs a, int layer,
                                                                        const int32_t* __restrict__ active,
                                                                        const int32_t* __restrict__ n_active,
                                                                        int max_active) {
-  constexpr int NW = kResolveThreads / 64;
-  __shared__ int s_miss[moe::kMaxE];
-  __shared__ int s_hits[NW], s_misses[NW];
-  __shared__ int64_t s_v[NW];
-  __shared__ int s_i[NW];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = min(max(*n_active, 0), max_active);
-  const int64_t clock = *a.clock;
-  const int64_t base = (int64_t)layer * a.E;
-  // hits: stamped in active order; misses: listed in active order (ascending id)
-  const bool valid = tid < n;
-  const int e = valid ? active[tid] : 0;
-  const int s = valid ? a.map[base + e] : -1;
-  const bool hit = valid && s >= 0, miss = valid && s < 0;
-  const uint64_t bh = __ballot(hit), bm = __ballot(miss);
-  const uint64_t below = (1ull << lane) - 1ull;
-  if (lane == 0) {
-    s_hits[wave] = __popcll(bh);
-    s_misses[wave] = __popcll(bm);
-  }
-  __syncthreads();
-  int hb = 0, mb = 0, nh = 0, nm = 0;
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) {
-      hb += s_hits[w];
-      mb += s_misses[w];
-    }
-    nh += s_hits[w];
-    nm += s_misses[w];
-  }
-  if (hit) a.stamp[s] = clock + 1 + hb + __popcll(bh & below);
-  if (miss) s_miss[mb + __popcll(bm & below)] = e;
-  __syncthreads();
-  uint64_t evictions = 0;
-  for (int j = 0; j < nm; ++j) {  // victim = smallest stamp; the stamps of this resolve are all larger
-    int64_t bv = INT64_MAX;
-    int bi = 0;
-    for (int q = tid; q < a.n_slots; q += kResolveThreads) {
-      const int64_t v = a.stamp[q];
-      if (v < bv) {
-        bv = v;
-        bi = q;
-      }
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-      const int64_t ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov < bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lane == 0) {
-      s_v[wave] = bv;
-      s_i[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < NW; ++w)
-        if (s_v[w] < bv || (s_v[w] == bv && s_i[w] < bi)) {
-          bv = s_v[w];
-          bi = s_i[w];
-        }
-      const int old = a.owner[bi];
-      if (old >= 0) {
-        a.map[old] = -1;
-        ++evictions;
-      }
-      const int idx = (int)(base + s_miss[j]);
-      a.owner[bi] = idx;
-      a.map[idx] = bi;
-      a.stamp[bi] = clock + 1 + nh + j;
-      a.copies[2 * j] = bi;
-      a.copies[2 * j + 1] = idx;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    *a.clock = clock + nh + nm;
-    *a.ncopies = nm;
-    a.stats[0] += (uint64_t)nh;
-    a.stats[1] += (uint64_t)nm;
-    a.stats[2] += (uint64_t)nm * a.expert_bytes;
-    a.stats[3] += 1;
-    a.stats[4] += evictions;
-  }
+  __shared__ moe::dev::SlotLds<kResolveThreads> S;
+  moe::dev::slot_resolve_block<kResolveThreads>(a, layer, active, min(max(*n_active, 0), max_active), S);
 }
 
 constexpr int kCopyThreads = 256, kCopyUnroll = 4;
@@ -549,7 +454,21 @@ moe_status moe_slot_table_resolve_device(moe_slot_table* t, int layer, const int
   if (max_active > t->n_slots)
     return fail(MOE_ECAPACITY, "moe_slot_table_resolve_device: up to " + std::to_string(max_active) +
                                    " active experts, " + std::to_string(t->n_slots) + " slots");
-  DevArgs a;
+  slot_resolve_kernel<<<1, kResolveThreads, 0, stream>>>(moe::slot_dev_args(t), layer, active, n_active, max_active);
+  if (moe_status st = moe::check_launch("slot_resolve")) return st;
+  return moe::launch_slot_copy(t, stream);
+}
+
+void moe_slot_table_destroy(moe_slot_table* t) { free_table(t); }
+
+}  // extern "C"
+
+namespace moe {
+
+bool slot_table_device_mode(const moe_slot_table* t) { return t && t->device_mode; }
+
+SlotDevArgs slot_dev_args(const moe_slot_table* t) {
+  SlotDevArgs a;
   a.map = t->slot_map_dev;
   a.owner = t->d_owner;
   a.stamp = t->d_stamp;
@@ -560,13 +479,17 @@ moe_status moe_slot_table_resolve_device(moe_slot_table* t, int layer, const int
   a.E = t->E;
   a.n_slots = t->n_slots;
   a.expert_bytes = t->expert_bytes;
-  slot_resolve_kernel<<<1, kResolveThreads, 0, stream>>>(a, layer, active, n_active, max_active);
-  if (moe_status st = moe::check_launch("slot_resolve")) return st;
-  slot_copy_kernel<<<kCopyGrid, kCopyThreads, 0, stream>>>(t->d_copies, t->d_ncopies, t->host_dev, t->slots,
-                                                            (int64_t)t->expert_bytes);
-  return moe::check_launch("slot_copy");
+  return a;
 }
 
-void moe_slot_table_destroy(moe_slot_table* t) { free_table(t); }
+SlotTableView slot_table_view(const moe_slot_table* t) {
+  return SlotTableView{t->L, t->E, t->n_slots, t->expert_bytes, t->slots, t->slot_map_dev};
+}
 
-}  // extern "C"
+moe_status launch_slot_copy(const moe_slot_table* t, hipStream_t stream) {
+  slot_copy_kernel<<<kCopyGrid, kCopyThreads, 0, stream>>>(t->d_copies, t->d_ncopies, t->host_dev, t->slots,
+                                                            (int64_t)t->expert_bytes);
+  return check_launch("slot_copy");
+}
+
+}  // namespace moe

@@ -267,6 +267,23 @@ moe_status moe_slot_table_map_host(const moe_slot_table* t, int32_t* out);
  * sequence of active sets.
  */
 size_t moe_slot_table_device_bytes(int L, int E, int n_slots);
+/*
+ * moe_layer_decode_slots -- moe_layer_decode through a slot table in device
+ * mode: the routing workgroup also resolves the routed experts of `layer`
+ * (moe_slot_table_resolve_device's policy), then the misses are copied in and
+ * the gate/up and down kernels run on the slots (four launches, or five when
+ * the combine cannot be folded).  q must be the table's view of `layer`:
+ * base = slots, stride = expert_bytes, slot_map = map + layer * E.  Outputs
+ * and workspace as moe_layer_decode (moe_layer_decode_workspace_bytes); every
+ * output is bit-identical to moe_layer_decode on resident weights.
+ * Errors: as moe_layer_decode; MOE_EINVAL if the table is not in device mode
+ * or q is not its view of `layer`; MOE_ECAPACITY if min(E, T*k) > n_slots.
+ */
+moe_status moe_layer_decode_slots(const moe_qlayer* q, moe_slot_table* t, int layer, const float* logits,
+                                  const void* x, moe_dtype x_t, int T, int k, const void* residual, moe_dtype r_t,
+                                  int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_assign,
+                                  int32_t* assign_pos, int32_t* active, int32_t* n_active, void* y, moe_dtype y_t,
+                                  float* out, uint16_t* out_bf16, void* ws, size_t ws_bytes, hipStream_t stream);
 moe_status moe_slot_table_enable_device(moe_slot_table* t, void* state, size_t state_bytes, hipStream_t stream);
 moe_status moe_slot_table_resolve_device(moe_slot_table* t, int layer, const int32_t* active,
                                          const int32_t* n_active, int max_active, hipStream_t stream);

@@ -233,3 +233,42 @@ def test_slot_table_device_mode_errors(moe):
         table.resolve(0, d)
     assert ei.value.status == 1
     table.close()
+
+
+@pytest.mark.parametrize("n_slots", [64, 30])
+def test_layer_decode_slots_matches_resident_layer_decode(moe, n_slots):
+    """moe_layer_decode_slots (router + resolve in one workgroup, copy, FFN) against moe_layer_decode on resident
+    weights, and the table's counters against the stand-alone device resolve on the same steps."""
+    import torch
+    w = _stack(H=2048, I=512, E=64, k=10)  # wide shape: the combine is folded into the down kernel
+    eb = w.expert_bytes
+    host = _host_master(w, torch)
+    dev_all = host.to("cuda")
+    resident = [moe.ExpertLayer(w.E, w.H, w.I, w.bits, dev_all, eb, base_offset=l * w.E * eb) for l in range(w.layers)]
+    tables = []
+    for _ in range(2):
+        slots = torch.empty(n_slots * eb, dtype=torch.uint8, device="cuda")
+        smap = torch.empty(w.layers * w.E, dtype=torch.int32, device="cuda")
+        t = moe.SlotTable(w.layers, w.E, n_slots, eb, host, slots, smap)
+        t.preload(_warm_pairs(w, n_slots))
+        t.enable_device()
+        tables.append(t)
+    fused, split = tables
+    for s in range(3):
+        x = torch.from_numpy(w.x(0, s).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        for l in range(w.layers):
+            lg = torch.from_numpy(synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, l, s), w.T, w.E,
+                                               synth.drifted_bias(w, l, s, 0.05))).cuda()
+            a = moe.layer_decode(resident[l], x, lg, w.k, residual=x)
+            b = moe.layer_decode_slots(fused, l, fused.layer(l, w.H, w.I, w.bits), x, lg, w.k, residual=x)
+            d = moe.dispatch(a[0], w.E)
+            split.resolve_device(l, d)
+            torch.cuda.synchronize()
+            for u, v in zip((a[0], a[1], a[3], a[4]), (b[0], b[1], b[3], b[4])):
+                assert np.array_equal(to_host(u).view(np.uint32), to_host(v).view(np.uint32)), (s, l)
+            x = a[4].to(torch.bfloat16)
+    assert fused.stats() == split.stats()
+    assert np.array_equal(fused.map_host(), split.map_host())
+    assert fused.stats()["misses"] > 0
+    for t in tables:
+        t.close()
