@@ -56,8 +56,8 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "d619ef0351924a89",
                     "fetch_kib": 7632.3, "write_kib": 62.9},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "0e606573d460d8b0", "fetch_kib": 362679.1,
-                    "write_kib": 93849.3},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "f852214076e49dd1", "fetch_kib": 359704.7,
+                    "write_kib": 143946.7},
 }
 
 
