@@ -28,11 +28,11 @@
 // permuted by row) with one barrier per step; global loads run kPrefetch steps
 // ahead, with no branch around them so that the compiler waits for one stage
 // only.  Workgroups are ordered so that the N-tiles of one M-tile run on the
-// same die and share its L2 copy of the gathered activation rows.  For gate/up
-// the 256 tile columns are 16 groups of 16: columns 0-7 of a group are gate
-// rows i0+8g .. i0+8g+7 and columns 8-15 the up rows of the same i, so in the
-// MFMA output layout (lane = column) gate and up of one i sit in lanes l and
-// l^8 and SwiGLU needs one lane swap.
+// same die and share its L2 copy of the gathered activation rows.  The MFMAs take
+// the weight fragment as their first operand, so the output comes transposed:
+// a lane holds 4 consecutive columns of one row, stored as one 8- or 16-byte
+// piece.  For gate/up the tile columns go in fours (gate i, gate i+1, up i,
+// up i+1), so SwiGLU stays inside a lane and h leaves as packed pairs.
 //
 // 2-bit decode uses a 4-entry fp16 table per (row, block): the packed pair of
 // codes (c_even, c_odd) in the two halfwords becomes a v_perm_b32 byte selector
@@ -277,11 +277,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   auto b_src = [&](int r, const uint8_t*& codes, const uint8_t*& sm) {
     int64_t row, oc, os;
     if constexpr (GATEUP) {
-      const int g = r / 16, jj = r % 16;
-      const int i = nt * (kBN / 2) + 8 * g + (jj & 7);
+      // column 4q + j of 16-column group g: j = 0, 1 -> gate rows i, i + 1; j = 2, 3 -> up rows i, i + 1
+      const int g = r / 16, q = (r % 16) / 4, jj = r % 4;
+      const int i = nt * (kBN / 2) + 8 * g + 2 * q + (jj & 1);
       row = i < A.I ? i : 0;
-      oc = jj < 8 ? A.off_c0 : A.off_c1;
-      os = jj < 8 ? A.off_s0 : A.off_s1;
+      oc = jj < 2 ? A.off_c0 : A.off_c1;
+      os = jj < 2 ? A.off_s0 : A.off_s1;
     } else {
       const int n = nt * kBN + r;
       row = n < A.H ? n : 0;
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
     for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj)
-        acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fi], bfr[fj], acc[fi][fj], 0, 0, 0);
+        acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[fj], af[fi], acc[fi][fj], 0, 0, 0);
   };
 
   // Software pipeline: global loads run DEPTH K-steps ahead of the MFMAs
@@ -389,31 +390,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
     }
   }
 
-  // ---- epilogue: lane = output column (lane & 15), rows 4*(lane >> 4) + r ----
-  const int col = lane & 15, rbase = 4 * (lane >> 4);
+  // ---- epilogue.  The MFMAs take the weights as their first operand, so a
+  // lane holds 4 consecutive output columns of one row: row 16 * fi + (lane & 15),
+  // columns 16 * fj + 4 * (lane >> 4) + r.
+  const int frow = lane & 15, fcol = 4 * (lane >> 4);
 #pragma unroll
-  for (int fi = 0; fi < FM; ++fi)
+  for (int fi = 0; fi < FM; ++fi) {
+    const int m = wm * (BM / 2) + 16 * fi + frow;
+    if (m >= rows) continue;
+    if constexpr (GATEUP) {
+      // columns 4q .. 4q + 3 = gate i, gate i + 1, up i, up i + 1
+      _Float16* hrow = reinterpret_cast<_Float16*>(A.out) + (size_t)(p_begin + m) * A.I;
 #pragma unroll
-    for (int fj = 0; fj < FN; ++fj)
+      for (int fj = 0; fj < FN; ++fj) {
+        const int i = nt * (kBN / 2) + 8 * (FN * wn + fj) + fcol / 2;
+        if (i >= A.I) continue;
+        const f32x4_t v = acc[fi][fj];
+        const float h0 = sat_f16(v[0] / (1.0f + expf(-v[0])) * v[2]);
+        const float h1 = sat_f16(v[1] / (1.0f + expf(-v[1])) * v[3]);
+        *reinterpret_cast<uint32_t*>(hrow + i) = pack_f16(h0, h1);
+      }
+    } else {
+      const int64_t a = A.sorted_assign[p_begin + m];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = acc[fi][fj][r];
-        const int m = wm * (BM / 2) + 16 * fi + rbase + r;
-        if constexpr (GATEUP) {
-          const float u = __shfl_xor(v, 8, 64);
-          const int i = nt * (kBN / 2) + 8 * (FN * wn + fj) + col;
-          if (col < 8 && m < rows && i < A.I)
-            reinterpret_cast<_Float16*>(A.out)[(size_t)(p_begin + m) * A.I + i] =
-                (_Float16)sat_f16(v / (1.0f + expf(-v)) * u);
+      for (int fj = 0; fj < FN; ++fj) {
+        const int n = nt * kBN + wn * (BN / 2) + 16 * fj + fcol;
+        if (n >= A.H) continue;
+        const f32x4_t v = acc[fi][fj];
+        if constexpr (YBF16) {
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<__bf16*>(A.out) + a * A.H + n) = make_uint2(lo, hi);
         } else {
-          const int n = nt * kBN + wn * (BN / 2) + 16 * fj + col;
-          if (m < rows && n < A.H) {
-            const int64_t a = A.sorted_assign[p_begin + m];
-            if constexpr (YBF16) reinterpret_cast<__bf16*>(A.out)[a * A.H + n] = (__bf16)v;
-            else reinterpret_cast<float*>(A.out)[a * A.H + n] = v;
-          }
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(A.out) + a * A.H + n) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
+    }
+  }
 }
 
 #ifndef MOE_MFMA_BM
