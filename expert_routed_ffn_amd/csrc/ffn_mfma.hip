@@ -71,6 +71,10 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {  // fp16 offset of 
   return row * kPitch + ((chunk ^ ((row >> SH) & 3)) * 8);
 }
 constexpr float kF16Max = 65504.0f;
+// Raw buffer resources: no range clamp (every access is in bounds by
+// construction), default data format for 32-bit elements.
+constexpr int kBufRecords = -1;
+constexpr int kBufFlags = 0x00020000;
 
 
 // Two floats -> packed fp16 pair (round to nearest even).
@@ -159,8 +163,14 @@ __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t* __restr
 }
 
 // x [n] (bf16 bits or fp32) -> fp16 (round to nearest even, saturating), 8 per thread.
+// Block 0 also clears the zero rows after x16 and h (z1, z2: 16-byte pieces).
 template <bool XF32>
-__global__ __launch_bounds__(256) void to_f16_kernel(const void* __restrict__ x, int64_t n8, uint4* __restrict__ out) {
+__global__ __launch_bounds__(256) void to_f16_kernel(const void* __restrict__ x, int64_t n8, uint4* __restrict__ out,
+                                                     uint4* __restrict__ z1, int n1, uint4* __restrict__ z2, int n2) {
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < n1; i += 256) z1[i] = make_uint4(0, 0, 0, 0);
+    for (int i = threadIdx.x; i < n2; i += 256) z2[i] = make_uint4(0, 0, 0, 0);
+  }
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
     float f[8];
     if constexpr (XF32) {
@@ -187,6 +197,7 @@ struct GemmArgs {
   int H, I, k;
   int64_t off_c0, off_s0, off_c1, off_s1;  // gate/up: Wg and Wu planes; down: Wd planes in c0/s0
   const _Float16* a_src;                   // x [T x H] (gate/up) or h [n x I] (down), fp16
+  int64_t a_zero_row;                      // T or n: an all-zero row of a_src
   const int32_t* offsets;
   const int32_t* sorted_assign;
   const int32_t* active;
@@ -201,7 +212,8 @@ struct GemmArgs {
 #ifndef MOE_MFMA_WAVES_PER_EU
 #define MOE_MFMA_WAVES_PER_EU 2
 #endif
-template <int BITS, int BM, int BN, bool GATEUP, bool YBF16>
+// PAIRB: the pair pipeline below (needs BN = 256 and K a multiple of 128).
+template <int BITS, int BM, int BN, bool GATEUP, bool YBF16, bool PAIRB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU))) void mfma_ffn_kernel(
     GemmArgs A) {
   constexpr int kBN = BN;
@@ -255,19 +267,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   // ---- A-tile sources: row pointer per chunk this thread copies --------------
   const uint8_t* a_row[A_CHUNKS];
   int a_col16[A_CHUNKS];
-  bool a_ok[A_CHUNKS];
 #pragma unroll
   for (int j = 0; j < A_CHUNKS; ++j) {
     const int c = tid + 256 * j;
     const int m = c / 4;
     a_col16[j] = c % 4;
-    a_ok[j] = m < rows;
-    const int p = p_begin + (a_ok[j] ? m : 0);
+    // rows past the tile's end read the all-zero row kept after the last source row
     if constexpr (GATEUP) {
-      const int64_t tok = A.sorted_assign[p] / A.k;
+      const int64_t tok = m < rows ? A.sorted_assign[p_begin + m] / A.k : A.a_zero_row;
       a_row[j] = reinterpret_cast<const uint8_t*>(A.a_src + tok * (int64_t)A.H);
     } else {
-      a_row[j] = reinterpret_cast<const uint8_t*>(A.a_src + (int64_t)p * A.I);
+      const int64_t p = m < rows ? p_begin + m : A.a_zero_row;
+      a_row[j] = reinterpret_cast<const uint8_t*>(A.a_src + p * A.I);
     }
   }
 
@@ -326,23 +337,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
     st.smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
   };
 
-  // A chunks and decoded B slice of stage `st` into LDS buffer `buf`.
-  auto store_stage = [&](const Stage& st, int buf) {
+  // A chunks of one K-step into LDS buffer `buf`.
+  auto store_a = [&](const uint4 (&a)[A_CHUNKS], int buf) {
 #pragma unroll
     for (int jj = 0; jj < A_CHUNKS; ++jj) {
       const int c = tid + 256 * jj;
       const int m = c / 4;
-      *reinterpret_cast<uint4*>(&lds_a[buf][lds_off(m, a_col16[jj])]) = a_ok[jj] ? st.a[jj] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&lds_a[buf][lds_off(m, a_col16[jj])]) = a[jj];
     }
+  };
+  // This thread's B slice of one K-step, decoded into LDS buffer `buf`.
+  auto store_b = [&](const uint32_t (&code)[B_HALVES][BITS / 2 == 1 ? 1 : 2], uint32_t smw, int buf) {
 #pragma unroll
     for (int hh = 0; hh < B_HALVES; ++hh) {
       uint32_t w[8];  // rows past I (or H) decode a valid row; their columns are never stored
-      if constexpr (BITS == 2) decode16_b2(st.code[hh][0], st.smw, w);
-      else decode16_b4(st.code[hh][0], st.code[hh][1], st.smw, w);
+      if constexpr (BITS == 2) decode16_b2(code[hh][0], smw, w);
+      else decode16_b4(code[hh][0], code[hh][1], smw, w);
       const int c0 = 2 * (b_half0 + hh);
       *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0)]) = make_uint4(w[0], w[1], w[2], w[3]);
       *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0 + 1)]) = make_uint4(w[4], w[5], w[6], w[7]);
     }
+  };
+  auto store_stage = [&](const Stage& st, int buf) {
+    store_a(st.a, buf);
+    store_b(st.code, st.smw, buf);
   };
 
   f32x4_t acc[FM][FN];
@@ -367,26 +385,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
         acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[fj], af[fi], acc[fi][fj], 0, 0, 0);
   };
 
-  // Software pipeline: global loads run DEPTH K-steps ahead of the MFMAs
-  // (stage s sits in st[s % DEPTH] from its load until its LDS store); LDS is
-  // double-buffered, one barrier per K-step.  The loop is unrolled by DEPTH so
-  // the register stages are static, and it has no branch around a load or a
-  // store: stages past the end reload the last K-step (never used), so every
-  // iteration issues the same loads and a store waits only for its own stage.
-  constexpr int DEPTH = kPrefetch;
-  Stage st[DEPTH];
+  static_assert(!PAIRB || B_HALVES == 2, "the pair pipeline needs a whole B row per thread");
+  if constexpr (PAIRB) {
+    {
+      // Pair pipeline: a thread owns a whole B row, so the codes of two K-steps
+      // are one (2-bit) or two (4-bit) 16-byte loads and their scale/min words
+      // one 8-byte load, a third of the per-K-step loads.  Stage s sits in LDS
+      // buffer s & 1; A runs two K-steps ahead in sa0/sa1 (even/odd stages), B
+      // pairs in bp0 (stages 4j, 4j+1) and bp1 (4j+2, 4j+3); loads past the end
+      // repeat the last K-step or pair and are never used.
+      struct BPair {
+        uint4 c[BITS / 2];
+        uint2 sm;
+      };
+      // Buffer loads: a 32-bit per-lane offset from a workgroup-uniform base,
+      // the K-step's offset in a scalar register (the host keeps every byte
+      // offset below 2^31 for this kernel).
+      const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16*>(A.a_src), (short)0, kBufRecords, kBufFlags);
+      const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(blob), (short)0, kBufRecords, kBufFlags);
+      const uint8_t* a_base = reinterpret_cast<const uint8_t*>(A.a_src);
+      int a_voff[A_CHUNKS];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_stage(st[d], min(d, KS - 1));
-  store_stage(st[0], 0);
-  __syncthreads();
-  for (int kb = 0; kb < KS; kb += DEPTH) {
+      for (int jj = 0; jj < A_CHUNKS; ++jj) a_voff[jj] = (int)(a_row[jj] - a_base) + a_col16[jj] * 16;
+      const int bc_voff = (int)(b_codes - blob), bs_voff = (int)(b_sm - blob);
+      auto load_a = [&](uint4 (&a)[A_CHUNKS], int ks) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int ks = kb + d;
-      load_stage(st[d], min(ks + DEPTH, KS - 1));  // st[d] held stage ks, already in LDS
-      if (ks < KS) mma_stage(ks & 1);
-      store_stage(st[(d + 1) % DEPTH], (ks + 1) & 1);
+        for (int jj = 0; jj < A_CHUNKS; ++jj)
+          a[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, a_voff[jj], ks * kBK * 2, 0));
+      };
+      auto load_bpair = [&](BPair& bp, int ks) {  // ks even, ks + 1 < KS
+#pragma unroll
+        for (int j = 0; j < BITS / 2; ++j)
+          bp.c[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bc_voff + 16 * j, ks * (4 * BITS), 0));
+        bp.sm = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bs_voff, ks * 4, 0));
+      };
+      auto store_bpair = [&](const BPair& bp, int e, int buf) {  // e: which K-step of the pair
+        uint32_t code[B_HALVES][BITS / 2 == 1 ? 1 : 2];
+        if constexpr (BITS == 2) {
+          code[0][0] = e ? bp.c[0].z : bp.c[0].x;
+          code[1][0] = e ? bp.c[0].w : bp.c[0].y;
+        } else {
+          const uint4 c = bp.c[e];
+          code[0][0] = c.x;
+          code[0][1] = c.y;
+          code[1][0] = c.z;
+          code[1][1] = c.w;
+        }
+        store_b(code, e ? bp.sm.y : bp.sm.x, buf);
+      };
+      uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
+      BPair bp0, bp1;
+      load_a(sa0, 0);
+      load_a(sa1, 1);
+      load_bpair(bp0, 0);
+      load_bpair(bp1, 2);
+      store_a(sa0, 0);
+      store_bpair(bp0, 0, 0);
       __syncthreads();
+      for (int kb = 0; kb < KS; kb += 4) {
+        load_a(sa0, min(kb + 2, KS - 1));
+        mma_stage(0);  // stage kb
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(sa1, 1);
+        store_bpair(bp0, 1, 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
+        load_a(sa1, min(kb + 3, KS - 1));
+        load_bpair(bp0, min(kb + 4, KS - 2));
+        mma_stage(1);  // stage kb + 1
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(sa0, 0);
+        store_bpair(bp1, 0, 0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
+        load_a(sa0, min(kb + 4, KS - 1));
+        mma_stage(0);  // stage kb + 2
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(sa1, 1);
+        store_bpair(bp1, 1, 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
+        load_a(sa1, min(kb + 5, KS - 1));
+        load_bpair(bp1, min(kb + 6, KS - 2));
+        mma_stage(1);  // stage kb + 3
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(sa0, 0);
+        store_bpair(bp0, 0, 0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
+      }
+    }
+  } else {
+    // Software pipeline: global loads run DEPTH K-steps ahead of the MFMAs
+    // (stage s sits in st[s % DEPTH] from its load until its LDS store); LDS is
+    // double-buffered, one barrier per K-step.  The loop is unrolled by DEPTH so
+    // the register stages are static, and it has no branch around a load or a
+    // store: stages past the end reload the last K-step (never used), so every
+    // iteration issues the same loads and a store waits only for its own stage.
+    constexpr int DEPTH = kPrefetch;
+    Stage st[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_stage(st[d], min(d, KS - 1));
+    store_stage(st[0], 0);
+    __syncthreads();
+    for (int kb = 0; kb < KS; kb += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int ks = kb + d;
+        load_stage(st[d], min(ks + DEPTH, KS - 1));  // st[d] held stage ks, already in LDS
+        if (ks < KS) mma_stage(ks & 1);
+        store_stage(st[(d + 1) % DEPTH], (ks + 1) & 1);
+        __syncthreads();
+      }
     }
   }
 
@@ -457,10 +569,10 @@ MfmaWs carve(uint8_t* ws, int T, int H, int n, int E, int I) {
   const int max_tiles = (int)ceil_div(n, kBM) + std::min(E, n);
   MfmaWs w;
   size_t off = 0;
-  w.x16 = reinterpret_cast<_Float16*>(ws + off);
-  off += up((size_t)T * H * 2);
-  w.h = reinterpret_cast<_Float16*>(ws + off);
-  off += up((size_t)n * I * 2);
+  w.x16 = reinterpret_cast<_Float16*>(ws + off);  // T rows, then one row of zeros
+  off += up((size_t)(T + 1) * H * 2);
+  w.h = reinterpret_cast<_Float16*>(ws + off);    // n rows, then one row of zeros
+  off += up((size_t)(n + 1) * I * 2);
   w.tiles = reinterpret_cast<TileInfo*>(ws + off);
   off += up((size_t)max_tiles * sizeof(TileInfo));
   w.count = reinterpret_cast<int32_t*>(ws + off);
@@ -479,11 +591,13 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   const MfmaWs W = carve(ws, T, q.H, n, q.E, q.I);
 
   const int64_t n8 = (int64_t)T * q.H / 8;
-  const int cblocks = (int)std::min<int64_t>(4096, ceil_div(n8, 256));
+  const int cblocks = (int)std::max<int64_t>(1, std::min<int64_t>(4096, ceil_div(n8, 256)));
+  uint4* z1 = reinterpret_cast<uint4*>(W.x16 + (size_t)T * q.H);
+  uint4* z2 = reinterpret_cast<uint4*>(W.h + (size_t)n * q.I);
   if (xf32)
-    to_f16_kernel<true><<<cblocks, 256, 0, s>>>(x, n8, reinterpret_cast<uint4*>(W.x16));
+    to_f16_kernel<true><<<cblocks, 256, 0, s>>>(x, n8, reinterpret_cast<uint4*>(W.x16), z1, q.H / 8, z2, q.I / 8);
   else
-    to_f16_kernel<false><<<cblocks, 256, 0, s>>>(x, n8, reinterpret_cast<uint4*>(W.x16));
+    to_f16_kernel<false><<<cblocks, 256, 0, s>>>(x, n8, reinterpret_cast<uint4*>(W.x16), z1, q.H / 8, z2, q.I / 8);
   if (moe_status st = check_launch("mfma_to_f16")) return st;
   mfma_tiles_kernel<<<1, 1024, 0, s>>>(offsets, active, n_active, kBM, W.tiles, W.count);
   if (moe_status st = check_launch("mfma_tiles")) return st;
@@ -507,21 +621,35 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   a.off_c1 = L.up_codes;
   a.off_s1 = L.up_sm;
   a.a_src = W.x16;
+  a.a_zero_row = T;
   a.n_tiles_n = (int)ceil_div(q.I, kBNGateUp / 2);
   a.out = W.h;
   const int tiles_pad = (int)ceil_div(max_tiles, kXcd) * kXcd;  // whole rounds over the dies
-  launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false>,
-           dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+  // The pair kernel addresses x, h and an expert blob with 32-bit byte offsets.
+  constexpr int64_t kOff = int64_t(1) << 31;
+  constexpr bool kPairOk = kBNGateUp == 256 && kBNDown == 256;
+  const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
+  if (kPairOk && off_ok && q.H % 128 == 0)
+    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+  else
+    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, false>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
   if (moe_status st = check_launch("mfma_gateup")) return st;
 
   // down: N = H in tiles of 128
   a.off_c0 = L.down_codes;
   a.off_s0 = L.down_sm;
   a.a_src = W.h;
+  a.a_zero_row = n;
   a.n_tiles_n = (int)ceil_div(q.H, kBNDown);
   a.out = y;
-  launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16>,
-           dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+  if (kPairOk && off_ok && q.I % 128 == 0)
+    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, kPairOk>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+  else
+    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, false>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
   return check_launch("mfma_down");
 }
 
