@@ -22,12 +22,17 @@
 // Both types run at the same MFMA rate on gfx950.
 //
 // Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile
-// (128 x 256); each wave owns (BM/2) x (BN/2) = 64 x 128, i.e. 4 x 8 fragments
-// of 16 x 16, so every fragment read from LDS feeds 4 to 8 MFMAs.  K-steps of
-// 32 go through double-buffered LDS tiles (64-byte rows, 16-byte chunks
-// permuted by row) with one barrier per step; global loads run kPrefetch steps
-// ahead, with no branch around them so that the compiler waits for one stage
-// only.  Workgroups are ordered so that the N-tiles of one M-tile run on the
+// (128 x 256); each wave owns 64 x 128, i.e. 4 x 8 fragments of 16 x 16, so
+// every fragment read from LDS feeds 4 to 8 MFMAs.  A wave's four 16-row
+// groups are interleaved with the other wave row's, and groups past the
+// tile's last row skip their MFMAs.  K-steps of 32 go through
+// double-buffered LDS tiles (64-byte rows, 16-byte chunks permuted by row)
+// with one barrier per step; global loads run two K-steps ahead, with no
+// branch around them so that the compiler waits for one stage only.  When K
+// is a multiple of 128 a thread fetches its B row's codes for two K-steps in
+// one 16-byte buffer load (the pair pipeline), with the K-step offset in a
+// scalar register.  Rows past a tile's end read an all-zero row kept after
+// the last row of x16 and of h.  Workgroups are ordered so that the N-tiles of one M-tile run on the
 // same die and share its L2 copy of the gathered activation rows.  The MFMAs take
 // the weight fragment as their first operand, so the output comes transposed:
 // a lane holds 4 consecutive columns of one row, stored as one 8- or 16-byte
@@ -59,10 +64,12 @@ constexpr int kXcd = 8;  // accelerator dies (each with its own L2) that workgro
 constexpr int kPrefetch = MOE_MFMA_PREFETCH;  // K-steps of global loads in flight ahead of the MFMAs
 // LDS tile rows: 0 = 80-byte pitch (padded); 1, 2 = 64-byte pitch with the
 // four 16-byte chunks of a row permuted by chunk ^ ((row >> SHIFT) & 3),
-// SHIFT = 2 or 1.  Layout 1 has a quarter fewer bank-conflict cycles than
-// the padded one on the prefill workload (same time) and a fifth less LDS.
+// SHIFT = 2 or 1.  Measured on gfx950 with 128-bit reads in the fragment
+// pattern (lane & 15 = row, lane >> 4 = chunk): layout 2 runs at about 200
+// bytes per clock per CU, layouts 0 and 1 at about 125; the row-per-lane
+// stores of the B tile run at about 75 in layout 2 and 64 in layout 1.
 #ifndef MOE_LDS_SWZ
-#define MOE_LDS_SWZ 1
+#define MOE_LDS_SWZ 2
 #endif
 constexpr int kPitch = MOE_LDS_SWZ == 0 ? 40 : 32;  // fp16 elements per LDS row
 __device__ __forceinline__ int lds_off(int row, int chunk) {  // fp16 offset of 16-byte chunk `chunk` of `row`
@@ -209,18 +216,24 @@ struct GemmArgs {
 
 // Two waves per SIMD (two workgroups per CU): the compiler keeps the 64 x 128
 // accumulator tile of a wave in VGPRs within that budget.
+#ifndef MOE_MFMA_INTERLEAVE
+#define MOE_MFMA_INTERLEAVE 0
+#endif
 #ifndef MOE_MFMA_WAVES_PER_EU
 #define MOE_MFMA_WAVES_PER_EU 2
 #endif
-// PAIRB: the pair pipeline below (needs BN = 256 and K a multiple of 128).
-template <int BITS, int BM, int BN, bool GATEUP, bool YBF16, bool PAIRB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU))) void mfma_ffn_kernel(
+// NT threads = NT / 64 waves in a (NT / 128) x 2 grid over the BM x BN tile.
+// PAIRB: the pair pipeline below (needs K a multiple of 128).
+template <int BITS, int BM, int BN, bool GATEUP, bool YBF16, bool PAIRB, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAVES_PER_EU))) void mfma_ffn_kernel(
     GemmArgs A) {
   constexpr int kBN = BN;
-  constexpr int FM = BM / 32;  // 16-row fragments per wave
-  constexpr int FN = BN / 32;  // 16-column fragments per wave
-  constexpr int A_CHUNKS = BM * 4 / 256;  // 16-byte chunks of the A tile per thread per K-step
-  constexpr int B_HALVES = BN / 128;      // 16-weight half rows of the B tile per thread per K-step
+  constexpr int WMR = NT / 128;           // wave rows
+  constexpr int FM = BM / (16 * WMR);     // 16-row fragments per wave
+  constexpr int FN = BN / 32;             // 16-column fragments per wave
+  constexpr int A_CHUNKS = BM * 4 / NT;   // 16-byte chunks of the A tile per thread per K-step
+  constexpr int B_HALVES = 2 * BN / NT;   // 16-weight half rows of the B tile per thread per K-step
+  static_assert(A_CHUNKS >= 1 && (B_HALVES == 1 || B_HALVES == 2), "tile and thread counts do not match");
   __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][BM * kPitch];
   __shared__ __attribute__((aligned(16))) _Float16 lds_b[2][kBN * kPitch];
 
@@ -237,13 +250,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   const int rows = min(BM, A.offsets[e + 1] - p_begin);
   const int idx = A.slot_map ? A.slot_map[e] : e;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = __builtin_amdgcn_readfirstlane(wave >> 1), wn = wave & 1;
+  // Wave row wm owns the 16-row groups wm, wm + WMR, wm + 2 WMR, ... of the
+  // tile (interleaved, so a partly filled tile loads the SIMDs evenly); its
+  // first nv fragments hold rows of the tile, the rest are skipped.
+  const int nv = max(0, min(FM, ((rows + 15) / 16 - wm + WMR - 1) / WMR));
   const int K = GATEUP ? A.H : A.I;
   const int KS = K / kBK;
 
   if (idx < 0) {  // expert not resident: NaN outputs, no weight reads
     const float nan = __builtin_nanf("");
-    for (int c = tid; c < BM * kBN; c += 256) {
+    for (int c = tid; c < BM * kBN; c += NT) {
       const int m = c / kBN, col = c % kBN;
       if (m >= rows) continue;
       if constexpr (GATEUP) {
@@ -269,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   int a_col16[A_CHUNKS];
 #pragma unroll
   for (int j = 0; j < A_CHUNKS; ++j) {
-    const int c = tid + 256 * j;
+    const int c = tid + NT * j;
     const int m = c / 4;
     a_col16[j] = c % 4;
     // rows past the tile's end read the all-zero row kept after the last source row
@@ -341,7 +358,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   auto store_a = [&](const uint4 (&a)[A_CHUNKS], int buf) {
 #pragma unroll
     for (int jj = 0; jj < A_CHUNKS; ++jj) {
-      const int c = tid + 256 * jj;
+      const int c = tid + NT * jj;
       const int m = c / 4;
       *reinterpret_cast<uint4*>(&lds_a[buf][lds_off(m, a_col16[jj])]) = a[jj];
     }
@@ -371,26 +388,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
 
   const int frag_r = lane & 15, frag_q = lane >> 4;  // row in the fragment, 16-byte chunk of K
   auto mma_stage = [&](int cur) {
+    if (nv == 0) return;
     f16x8_t af[FM], bfr[FN];
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi)
-      af[fi] = *reinterpret_cast<const f16x8_t*>(&lds_a[cur][lds_off(wm * (BM / 2) + 16 * fi + frag_r, frag_q)]);
+      af[fi] = *reinterpret_cast<const f16x8_t*>(&lds_a[cur][lds_off(16 * (wm + WMR * fi) + frag_r, frag_q)]);
 #pragma unroll
     for (int fj = 0; fj < FN; ++fj)
       bfr[fj] = *reinterpret_cast<const f16x8_t*>(&lds_b[cur][lds_off(wn * (BN / 2) + 16 * fj + frag_r, frag_q)]);
 #pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
+    for (int fi = 0; fi < FM; ++fi) {
+      if (fi >= nv) break;
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj)
         acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bfr[fj], af[fi], acc[fi][fj], 0, 0, 0);
+    }
   };
 
-  static_assert(!PAIRB || B_HALVES == 2, "the pair pipeline needs a whole B row per thread");
   if constexpr (PAIRB) {
     {
-      // Pair pipeline: a thread owns a whole B row, so the codes of two K-steps
-      // are one (2-bit) or two (4-bit) 16-byte loads and their scale/min words
-      // one 8-byte load, a third of the per-K-step loads.  Stage s sits in LDS
+      // Pair pipeline: the codes of a B row for two K-steps are one (2-bit) or
+      // two (4-bit) 16-byte loads and their scale/min words one 8-byte load (the
+      // two threads that share a row when NT = 2 BN load the same bytes).  Stage s sits in LDS
       // buffer s & 1; A runs two K-steps ahead in sa0/sa1 (even/odd stages), B
       // pairs in bp0 (stages 4j, 4j+1) and bp1 (4j+2, 4j+3); loads past the end
       // repeat the last K-step or pair and are never used.
@@ -423,17 +442,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
       };
       auto store_bpair = [&](const BPair& bp, int e, int buf) {  // e: which K-step of the pair
         uint32_t code[B_HALVES][BITS / 2 == 1 ? 1 : 2];
-        if constexpr (BITS == 2) {
-          code[0][0] = e ? bp.c[0].z : bp.c[0].x;
-          code[1][0] = e ? bp.c[0].w : bp.c[0].y;
-        } else {
-          const uint4 c = bp.c[e];
-          code[0][0] = c.x;
-          code[0][1] = c.y;
-          code[1][0] = c.z;
-          code[1][1] = c.w;
+        if constexpr (B_HALVES == 2) {
+          if constexpr (BITS == 2) {
+            code[0][0] = e ? bp.c[0].z : bp.c[0].x;
+            code[1][0] = e ? bp.c[0].w : bp.c[0].y;
+          } else {
+            const uint4 c = bp.c[e];
+            code[0][0] = c.x;
+            code[0][1] = c.y;
+            code[1][0] = c.z;
+            code[1][1] = c.w;
+          }
+        } else {  // two threads per row: each decodes its half, b_half0
+          if constexpr (BITS == 2) {
+            const uint32_t lo = e ? bp.c[0].z : bp.c[0].x, hi = e ? bp.c[0].w : bp.c[0].y;
+            code[0][0] = b_half0 ? hi : lo;
+          } else {
+            const uint4 c = bp.c[e];
+            code[0][0] = b_half0 ? c.z : c.x;
+            code[0][1] = b_half0 ? c.w : c.y;
+          }
         }
         store_b(code, e ? bp.sm.y : bp.sm.x, buf);
+      };
+      // MOE_MFMA_INTERLEAVE = V > 0: the decode of the next stage is spread over
+      // the MFMAs (one MFMA, then V VALU ops, 32 times), LDS writes last;
+      // 0: a fence after the MFMAs keeps the decode behind them.
+      auto mfma_fence = [] {
+        if constexpr (MOE_MFMA_INTERLEAVE == 0) __builtin_amdgcn_sched_barrier(0);
+      };
+      auto step_hint = [] {
+        if constexpr (MOE_MFMA_INTERLEAVE > 0) {
+          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);  // fragment reads
+#pragma unroll
+          for (int i = 0; i < FM * FN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, MOE_MFMA_INTERLEAVE, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // LDS writes
+        }
       };
       uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
       BPair bp0, bp1;
@@ -447,32 +494,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
       for (int kb = 0; kb < KS; kb += 4) {
         load_a(sa0, min(kb + 2, KS - 1));
         mma_stage(0);  // stage kb
-        __builtin_amdgcn_sched_barrier(0);
+        mfma_fence();
         store_a(sa1, 1);
         store_bpair(bp0, 1, 1);
+        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
         load_a(sa1, min(kb + 3, KS - 1));
         load_bpair(bp0, min(kb + 4, KS - 2));
         mma_stage(1);  // stage kb + 1
-        __builtin_amdgcn_sched_barrier(0);
+        mfma_fence();
         store_a(sa0, 0);
         store_bpair(bp1, 0, 0);
+        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
         load_a(sa0, min(kb + 4, KS - 1));
         mma_stage(0);  // stage kb + 2
-        __builtin_amdgcn_sched_barrier(0);
+        mfma_fence();
         store_a(sa1, 1);
         store_bpair(bp1, 1, 1);
+        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
         load_a(sa1, min(kb + 5, KS - 1));
         load_bpair(bp1, min(kb + 6, KS - 2));
         mma_stage(1);  // stage kb + 3
-        __builtin_amdgcn_sched_barrier(0);
+        mfma_fence();
         store_a(sa0, 0);
         store_bpair(bp0, 0, 0);
+        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
       }
@@ -508,7 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   const int frow = lane & 15, fcol = 4 * (lane >> 4);
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi) {
-    const int m = wm * (BM / 2) + 16 * fi + frow;
+    const int m = 16 * (wm + WMR * fi) + frow;
     if (m >= rows) continue;
     if constexpr (GATEUP) {
       // columns 4q .. 4q + 3 = gate i, gate i + 1, up i, up i + 1
@@ -543,6 +594,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
   }
 }
 
+// 128 x 256 tiles with 256 threads (two workgroups per CU).  256 x 256 tiles
+// with 512 threads share one decoded B tile between twice the rows (a third
+// fewer M-tiles on the prefill workload) but measured no faster.
 #ifndef MOE_MFMA_BM
 #define MOE_MFMA_BM 128
 #endif
@@ -555,6 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WA
 constexpr int kBM = MOE_MFMA_BM;
 constexpr int kBNGateUp = MOE_MFMA_BN_GU;
 constexpr int kBNDown = MOE_MFMA_BN_DN;
+constexpr int kNT = 2 * kBM;  // one wave per 64 x 128 piece of the tile
 
 struct MfmaWs {
   _Float16* x16;
@@ -627,14 +682,14 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   const int tiles_pad = (int)ceil_div(max_tiles, kXcd) * kXcd;  // whole rounds over the dies
   // The pair kernel addresses x, h and an expert blob with 32-bit byte offsets.
   constexpr int64_t kOff = int64_t(1) << 31;
-  constexpr bool kPairOk = kBNGateUp == 256 && kBNDown == 256;
+  constexpr bool kPairOk = true;
   const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
   if (kPairOk && off_ok && q.H % 128 == 0)
-    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk>,
-             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk, kNT>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
-    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, false>,
-             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, false, kNT>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   if (moe_status st = check_launch("mfma_gateup")) return st;
 
   // down: N = H in tiles of 128
@@ -645,11 +700,11 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   a.n_tiles_n = (int)ceil_div(q.H, kBNDown);
   a.out = y;
   if (kPairOk && off_ok && q.I % 128 == 0)
-    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, kPairOk>,
-             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, kPairOk, kNT>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
-    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, false>,
-             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(256), 0, s, a);
+    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, false, kNT>,
+             dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   return check_launch("mfma_down");
 }
 
