@@ -56,8 +56,8 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "d619ef0351924a89",
                     "fetch_kib": 7632.3, "write_kib": 62.9},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "f852214076e49dd1", "fetch_kib": 359704.7,
-                    "write_kib": 143946.7},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "344d26f0b49b6274", "fetch_kib": 384532.0,
+                    "write_kib": 88696.5},
 }
 
 
