@@ -53,6 +53,7 @@ def lib():
         L.oracle_ffn_decoded.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
         L.oracle_expert_ffn.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.oracle_combine.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+        L.oracle_router_logits.argtypes = [vp, i32, vp, i32, i32, i32, vp]
         L.oracle_layer.restype = i32
         L.oracle_layer.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         _lib = L
@@ -145,6 +146,25 @@ def combine(y: np.ndarray, w: np.ndarray, residual: np.ndarray | None = None) ->
     r = None if residual is None else np.ascontiguousarray(residual, np.float64)
     out = np.empty((T, H), np.float64)
     lib().oracle_combine(_p(y), _p(w), T, k, H, _p(r), _p(out))
+    return out
+
+
+def router_logits(x: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
+    """Router projection logits [T, E] (float64) of x (float32 values or uint16 raw bf16 bits, [T, H])
+    and router weights wr_bits (uint16 raw bf16 bits, [E, H])."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        xb = 1
+    elif x.dtype == np.float32:
+        xb = 0
+    else:
+        raise TypeError("x must be float32 values or uint16 bf16 bits")
+    wr = np.ascontiguousarray(wr_bits, np.uint16)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape == (E, H)
+    out = np.empty((T, E), np.float64)
+    lib().oracle_router_logits(_p(x), xb, _p(wr), T, H, E, _p(out))
     return out
 
 

@@ -253,6 +253,25 @@ static double x_value(const void* x, int x_is_bf16, int64_t i) {
   return x_is_bf16 ? oracle_bf16(((const uint16_t*)x)[i]) : (double)((const float*)x)[i];
 }
 
+/* ---- router projection ------------------------------------------------------ */
+
+/* The router scores every expert from the token's hidden state (Strata feature,
+ * tech.hub77a.com, section "2. 왜 대단한가" (2): the router's choice decides which
+ * experts run).  The pages give no formula; the reading taken is a bias-free
+ * linear map: logits[t][e] = sum_c x[t][c] * Wr[e][c].
+ * x: [T x H] fp32 values (x_is_bf16 = 0) or raw bf16 bits (x_is_bf16 = 1);
+ * wr: [E x H] raw bf16 bits; logits: [T x E] doubles. */
+void oracle_router_logits(const void* x, int x_is_bf16, const uint16_t* wr, int T, int H, int E, double* logits) {
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int c = 0; c < H; ++c)
+        acc += x_value(x, x_is_bf16, (int64_t)t * H + c) * oracle_bf16(wr[(int64_t)e * H + c]);
+      logits[(int64_t)t * E + e] = acc;
+    }
+}
+
+
 /* x: [T x H] fp32 values (x_is_bf16 = 0) or raw bf16 bits (x_is_bf16 = 1).
  * experts: expert e's blob at experts + e * stride.
  * residual: NULL or [T x H] doubles.

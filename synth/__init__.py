@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
-TAG_LOGITS, TAG_X, TAG_WEIGHT, TAG_RANK, TAG_DRIFT = 1, 2, 3, 4, 5
+TAG_LOGITS, TAG_X, TAG_WEIGHT, TAG_RANK, TAG_DRIFT, TAG_ROUTER = 1, 2, 3, 4, 5, 6
 
 
 def build(force: bool = True) -> str:
@@ -53,6 +53,7 @@ def lib():
         L.synth_f64_to_f16.argtypes = [dbl]
         L.synth_normal_f32.argtypes = [u64, i64, flt, vp]
         L.synth_normal_bf16.argtypes = [u64, i64, vp]
+        L.synth_normal_bf16_scaled.argtypes = [u64, i64, dbl, vp]
         L.synth_ranks.argtypes = [u64, i32, vp]
         L.synth_zipf_bias.argtypes = [u64, i32, dbl, vp]
         L.synth_logits.argtypes = [u64, i32, i32, vp, vp]
@@ -105,6 +106,13 @@ def normal_bf16_bits(key: int, shape) -> np.ndarray:
     """bf16 (round-to-nearest-even of fp32 N(0,1)) as raw uint16 bits."""
     out = np.empty(shape, np.uint16)
     lib().synth_normal_bf16(key, out.size, _p(out))
+    return out
+
+
+def normal_bf16_bits_scaled(key: int, shape, scale: float) -> np.ndarray:
+    """bf16 (round-to-nearest-even of fp32 scale * N(0,1)) as raw uint16 bits."""
+    out = np.empty(shape, np.uint16)
+    lib().synth_normal_bf16_scaled(key, out.size, float(scale), _p(out))
     return out
 
 
@@ -209,6 +217,12 @@ class Workload:
         if self.x_dtype == "f32":
             return normal_f32(key, (self.T, self.H))
         return normal_bf16_bits(key, (self.T, self.H))
+
+    def router(self, layer: int = 0) -> np.ndarray:
+        """Router weights [E, H] as raw bf16 bits: N(0, 1/H) entries, so that with
+        N(0,1) activations every logit has unit variance."""
+        return normal_bf16_bits_scaled(stream_key(self.seed, TAG_ROUTER, layer), (self.E, self.H),
+                                       1.0 / np.sqrt(self.H))
 
     def experts(self, layer: int = 0, which=None, nthreads=None) -> np.ndarray:
         return layer_experts(self.seed, layer, self.E, self.H, self.I, self.bits, self.std, which, nthreads)

@@ -134,6 +134,11 @@ void synth_normal_bf16(uint64_t key, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne((float)draw_normal(key, (uint64_t)i));
 }
 
+/* out[i] = bf16_rne(fp32(scale * N(0,1))) as raw bits. */
+void synth_normal_bf16_scaled(uint64_t key, int64_t n, double scale, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne((float)(draw_normal(key, (uint64_t)i) * scale));
+}
+
 /* Seeded permutation of ranks 1..E (Fisher-Yates driven by the stream). */
 void synth_ranks(uint64_t key, int E, int32_t* rank) {
   for (int e = 0; e < E; ++e) rank[e] = e + 1;
@@ -209,7 +214,7 @@ void synth_quantize_matrix(const double* w, int R, int K, int bits, uint32_t* co
 }
 
 /* Stream tags. */
-enum { TAG_LOGITS = 1, TAG_X = 2, TAG_WEIGHT = 3, TAG_RANK = 4, TAG_DRIFT = 5 };
+enum { TAG_LOGITS = 1, TAG_X = 2, TAG_WEIGHT = 3, TAG_RANK = 4, TAG_DRIFT = 5, TAG_ROUTER = 6 };
 
 /* One expert: Wg, Wu [I x H] and Wd [H x I] from N(0, std), encoded into blob. */
 void synth_expert(uint64_t seed, int layer, int expert, int H, int I, int bits, double std, uint8_t* blob) {

@@ -343,3 +343,66 @@ def test_bf16_input_rows_decode_like_float32():
     ra = oracle.layer(xb, lg, ex, 2, 64, 32, 2)
     rb = oracle.layer(as_f32, lg, ex, 2, 64, 32, 2)
     assert np.array_equal(ra["out"], rb["out"])
+
+
+# ---- router projection ------------------------------------------------------
+
+def _bf16_bits(values) -> np.ndarray:
+    """Raw bf16 bits of values that bf16 holds exactly (checked)."""
+    f = np.asarray(values, np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), f), "value not exact in bf16"
+    return bits
+
+
+def test_router_one_hot_rows_pick_their_column():
+    rng = np.random.default_rng(7)
+    T, H, E = 5, 96, 12
+    cols = rng.permutation(H)[:E]
+    wr = np.zeros((E, H), np.float32)
+    wr[np.arange(E), cols] = 1.0
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    got = oracle.router_logits(x, _bf16_bits(wr))
+    assert np.array_equal(got, x[:, cols].astype(np.float64))
+
+
+def test_router_constant_rows_scale_the_row_sum():
+    rng = np.random.default_rng(8)
+    T, H, E = 4, 64, 6
+    c = np.array([0.5, -2.0, 3.0, 0.0, -0.25, 8.0], np.float32)
+    wr = np.repeat(c[:, None], H, axis=1)
+    x = rng.integers(-8, 9, (T, H)).astype(np.float32)  # small integers: every sum is exact
+    got = oracle.router_logits(x, _bf16_bits(wr))
+    want = np.outer(x.astype(np.float64).sum(axis=1), c.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_router_swapping_operands_transposes_the_logits():
+    key_a, key_b = synth.stream_key(3, synth.TAG_ROUTER, 1), synth.stream_key(3, synth.TAG_ROUTER, 2)
+    a = synth.normal_bf16_bits(key_a, (7, 64))
+    b = synth.normal_bf16_bits(key_b, (9, 64))
+    ab = oracle.router_logits(a, b)
+    ba = oracle.router_logits(b, a)
+    assert ab.shape == (7, 9) and np.array_equal(ab, ba.T)
+
+
+def test_router_is_linear_in_the_weights_and_tokens_are_independent():
+    rng = np.random.default_rng(9)
+    T, H, E = 6, 32, 5
+    w1 = rng.integers(-4, 5, (E, H)).astype(np.float32)
+    w2 = rng.integers(-4, 5, (E, H)).astype(np.float32)
+    x = rng.integers(-6, 7, (T, H)).astype(np.float32)
+    l1 = oracle.router_logits(x, _bf16_bits(w1))
+    l2 = oracle.router_logits(x, _bf16_bits(w2))
+    l12 = oracle.router_logits(x, _bf16_bits(w1 + w2))
+    assert np.array_equal(l1 + l2, l12)
+    # a token's logits do not depend on the other tokens
+    assert np.array_equal(oracle.router_logits(x[2:3], _bf16_bits(w1)), l1[2:3])
+
+
+def test_router_bf16_tokens_decode_like_float32():
+    key = synth.stream_key(4, synth.TAG_X, 0)
+    xb = synth.normal_bf16_bits(key, (3, 64))
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    wr = synth.normal_bf16_bits(synth.stream_key(4, synth.TAG_ROUTER, 0), (10, 64))
+    assert np.array_equal(oracle.router_logits(xb, wr), oracle.router_logits(xf, wr))

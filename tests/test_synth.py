@@ -67,3 +67,13 @@ def test_drift_walk_matches_drifted_bias():
     for s in range(6):
         assert np.array_equal(walk[s], synth.drifted_bias(w, 3, s, 0.05))
     assert not np.array_equal(walk[0], walk[5])
+
+
+def test_router_weights_are_seeded_bf16_with_unit_logit_variance():
+    w = synth.decode_verify()
+    a, b = w.router(0), w.router(0)
+    assert a.dtype == np.uint16 and a.shape == (w.E, w.H)
+    assert np.array_equal(a, b) and not np.array_equal(a, w.router(1))
+    vals = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    # N(0, 1/H) entries: H * var is 1 within sampling error
+    assert abs(vals.var() * w.H - 1.0) < 0.01
