@@ -56,6 +56,10 @@ def _load():
     L.moe_expert_bytes.argtypes = [i32, i32, i32]
     L.moe_route_topk.restype = st
     L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    L.moe_router_logits.restype = st
+    L.moe_router_logits.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
+    L.moe_router_topk.restype = st
+    L.moe_router_topk.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp, vp, vp]
     L.moe_dispatch_workspace_bytes.restype = sz
     L.moe_dispatch_workspace_bytes.argtypes = [i32, i32, i32]
     L.moe_dispatch.restype = st
@@ -145,7 +149,7 @@ def _need(t: torch.Tensor, name: str):
 
 
 KERNELS = {"route": 0, "dispatch": 1, "gemv_gateup": 2, "gemv_down": 3, "mfma_gateup": 4, "mfma_down": 5,
-           "combine": 6, "decode_prep": 7}
+           "combine": 6, "decode_prep": 7, "router": 8}
 
 
 def profile_next_launch(kernel: str, start, stop):
@@ -174,6 +178,42 @@ def route_topk(logits: torch.Tensor, k: int, ids: torch.Tensor | None = None, w:
         w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check(lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream, logits.device)))
     return ids, w
+
+
+# ---- router projection ----------------------------------------------------------------
+
+def router_logits(x: torch.Tensor, w_r: torch.Tensor, logits: torch.Tensor | None = None, stream=None):
+    """logits [T, E] fp32 = x [T, H] (fp32 or bf16) . w_r [E, H] (bf16)^T."""
+    _need(x, "x")
+    _need(w_r, "w_r")
+    if w_r.dtype != torch.bfloat16:
+        raise TypeError("w_r must be bfloat16")
+    T, H = x.shape
+    E = w_r.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib.moe_router_logits(_ptr(x), _dtype_code(x), _ptr(w_r), T, H, E, _ptr(logits),
+                                 _stream(stream, x.device)))
+    return logits
+
+
+def router_topk(x: torch.Tensor, w_r: torch.Tensor, k: int, logits: torch.Tensor | None = None,
+                ids: torch.Tensor | None = None, w: torch.Tensor | None = None, stream=None):
+    """Router projection then top-k: (logits, ids, w)."""
+    _need(x, "x")
+    _need(w_r, "w_r")
+    T, H = x.shape
+    E = w_r.shape[0]
+    dev = x.device
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib.moe_router_topk(_ptr(x), _dtype_code(x), _ptr(w_r), T, H, E, k, _ptr(logits), _ptr(ids), _ptr(w),
+                               _stream(stream, dev)))
+    return logits, ids, w
 
 
 # ---- moe_dispatch ------------------------------------------------------------------

@@ -109,6 +109,29 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* ids
   return launch_route_topk(logits, T, E, k, ids, w, stream);
 }
 
+moe_status moe_router_logits(const void* x, moe_dtype x_t, const void* w_r, int T, int H, int E, float* logits,
+                             hipStream_t stream) {
+  if (T < 0) return fail(MOE_EINVAL, "moe_router_logits: T < 0");
+  if (x_t != MOE_F32 && x_t != MOE_BF16) return fail(MOE_EINVAL, "moe_router_logits: bad x dtype");
+  if (E < 1 || E > kMaxE) return fail(MOE_EUNSUPPORTED, fmt("moe_router_logits: E = %d outside 1..%d", E, kMaxE));
+  if (H < 32 || H > 16384 || H % 32 != 0)
+    return fail(MOE_EUNSUPPORTED, fmt("moe_router_logits: H = %d (needs a multiple of 32 in 32..16384)", H));
+  if (T == 0) return MOE_OK;
+  if (!x || !w_r || !logits) return fail(MOE_EINVAL, "moe_router_logits: null pointer");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_r)) & 15)
+    return fail(MOE_EINVAL, "moe_router_logits: x and w_r must be 16-byte aligned");
+  return launch_router_logits(x, x_t == MOE_F32, reinterpret_cast<const uint16_t*>(w_r), T, H, E, logits, stream);
+}
+
+moe_status moe_router_topk(const void* x, moe_dtype x_t, const void* w_r, int T, int H, int E, int k, float* logits,
+                           int32_t* ids, float* w, hipStream_t stream) {
+  if (moe_status st = check_ek("moe_router_topk", E, k)) return st;
+  if (T > 0 && (!ids || !w)) return fail(MOE_EINVAL, "moe_router_topk: null pointer");
+  if (moe_status st = moe_router_logits(x, x_t, w_r, T, H, E, logits, stream)) return st;
+  if (T == 0) return MOE_OK;
+  return launch_route_topk(logits, T, E, k, ids, w, stream);
+}
+
 size_t moe_dispatch_workspace_bytes(int T, int k, int E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   return dispatch_ws_bytes(T * k, E);

@@ -33,6 +33,9 @@ constexpr int kMaxK = 16;
 
 moe_status launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 
+moe_status launch_router_logits(const void* x, bool xf32, const uint16_t* wr, int T, int H, int E, float* logits,
+                                hipStream_t s);
+
 size_t dispatch_ws_bytes(int n, int E);
 moe_status launch_dispatch(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* sorted_assign,
                            int32_t* assign_pos, int32_t* active, int32_t* n_active, void* ws, hipStream_t s);

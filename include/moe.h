@@ -115,6 +115,31 @@ size_t moe_expert_bytes(int H, int I, int bits);
 moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t stream);
 
 /*
+ * moe_router_logits -- the router projection that produces the logits.
+ * Passage: Strata feature, section "2. 왜 대단한가" (2) (the router's choice
+ * decides which experts run).  The pages give no formula; the projection is a
+ * bias-free linear map: logits[t][e] = sum_c x[t][c] * w_r[e][c].
+ *   x       [T x H] device, fp32 or bf16 (x_t), row-major, 16-byte aligned.
+ *   w_r     [E x H] device, bf16 bits (uint16), row-major, 16-byte aligned.
+ *   logits  [T x E] fp32 out, row-major.
+ * Products and sums in fp32 (a bf16 product is exact in fp32).  bf16 x with
+ * T >= 64 runs a bf16 MFMA GEMM; otherwise one wave per expert row (a GEMV
+ * over up to 16 tokens per pass).  No workspace.
+ * Errors: MOE_EINVAL (null pointers with T > 0, T < 0, bad dtype),
+ * MOE_EUNSUPPORTED (E, H out of the library limits).
+ */
+moe_status moe_router_logits(const void* x, moe_dtype x_t, const void* w_r, int T, int H, int E, float* logits,
+                             hipStream_t stream);
+
+/*
+ * moe_router_topk -- moe_router_logits, then moe_route_topk on its logits.
+ * logits is a caller buffer [T x E] fp32 that receives the logits; ids and w
+ * as for moe_route_topk.  Two launches on `stream`.
+ */
+moe_status moe_router_topk(const void* x, moe_dtype x_t, const void* w_r, int T, int H, int E, int k, float* logits,
+                           int32_t* ids, float* w, hipStream_t stream);
+
+/*
  * moe_dispatch -- group the n = T*k assignments a = t*k + j by expert.
  * Passage: the tokens routed to one expert are computed together (Strata
  * feature, section "2. 왜 대단한가" (2): the compute path follows the routing).
@@ -305,7 +330,8 @@ typedef enum moe_kernel {
   MOE_KERNEL_DECODE_PREP = 7, /* descriptor preparation of the stand-alone GEMV path */
   MOE_KERNEL_MFMA_GATEUP = 4,
   MOE_KERNEL_MFMA_DOWN = 5,
-  MOE_KERNEL_COMBINE = 6
+  MOE_KERNEL_COMBINE = 6,
+  MOE_KERNEL_ROUTER = 8 /* router projection (GEMV or MFMA) */
 } moe_kernel;
 moe_status moe_profile_next_launch(moe_kernel kernel, hipEvent_t start, hipEvent_t stop);
 

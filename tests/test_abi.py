@@ -119,3 +119,24 @@ def test_auto_path_workspace_follows_routed_rows():
         want = GEMV if T * k <= 256 else MFMA
         assert ws(T, k, AUTO) == ws(T, k, want), (T, k)
     assert ws(26, 10, GEMV) != ws(26, 10, MFMA)
+
+
+def test_router_argument_checks():
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)  # 8-byte aligned only
+    F32, BF16 = _lib.MOE_F32, _lib.MOE_BF16
+    assert _st(L.moe_router_logits(NULL, BF16, NULL, -1, 64, 8, NULL, NULL)) == _lib.MOE_EINVAL
+    assert _st(L.moe_router_logits(NULL, 7, NULL, 3, 64, 8, NULL, NULL)) == _lib.MOE_EINVAL
+    assert _st(L.moe_router_logits(NULL, BF16, NULL, 3, 64, 0, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_router_logits(NULL, BF16, NULL, 3, 64, 1025, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_router_logits(NULL, BF16, NULL, 3, 48, 8, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_router_logits(NULL, F32, NULL, 3, 32768, 8, NULL, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_router_logits(NULL, BF16, NULL, 0, 64, 8, NULL, NULL)) == _lib.MOE_OK
+    assert _st(L.moe_router_logits(fake, BF16, NULL, 3, 64, 8, fake, NULL)) == _lib.MOE_EINVAL
+    assert _st(L.moe_router_logits(odd, BF16, fake, 3, 64, 8, fake, NULL)) == _lib.MOE_EINVAL
+    assert b"aligned" in L.moe_last_error()
+    # the top-k wrapper checks E and k first, then the projection's arguments
+    assert _st(L.moe_router_topk(fake, BF16, fake, 3, 64, 8, 9, fake, fake, fake, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_router_topk(fake, BF16, fake, 3, 64, 8, 2, fake, NULL, fake, NULL)) == _lib.MOE_EINVAL
+    assert _st(L.moe_router_topk(fake, BF16, fake, 3, 48, 8, 2, fake, fake, fake, NULL)) == _lib.MOE_EUNSUPPORTED
+    assert _st(L.moe_router_topk(NULL, BF16, NULL, 0, 64, 8, 2, NULL, NULL, NULL, NULL)) == _lib.MOE_OK
