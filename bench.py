@@ -334,6 +334,50 @@ def prefill_bench(args, torch, moe, synth, oracle):
     }
 
 
+def router_bench(args, torch, moe, synth, oracle):
+    """Router projection: decode step (T=3, GEMV) over rotated weight copies, and a prefill chunk
+    (T=8192, MFMA)."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    wd, wp = synth.decode_verify(), synth.prefill(args.prefill_bias)
+    E, H = wd.E, wd.H
+    copies = 160  # 160 x 2 MB: more than the last-level cache, so each launch streams from HBM
+    wr_np = wd.router()
+    wr = torch.from_numpy(wr_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    wrs = wr.unsqueeze(0).repeat(copies, 1, 1).contiguous()
+    res = {}
+    for name, w, n in (("decode", wd, 4 * copies), ("prefill", wp, 20)):
+        x_np = w.x()
+        x = torch.from_numpy(x_np.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        logits = torch.empty((w.T, E), dtype=torch.float32, device=dev)
+        moe.router_logits(x, wrs[0], logits)
+        torch.cuda.synchronize()
+        rows = np.array([0, w.T - 1])
+        ref = oracle.router_logits(x_np[rows], wr_np)
+        err = float(np.abs(logits.cpu().numpy()[rows].astype(np.float64) - ref).max())
+        if err > 1e-3:
+            raise SystemExit(f"bench: router logits do not match the oracle ({err:.3e})")
+        for i in range(copies):
+            moe.router_logits(x, wrs[i % copies], logits)
+        timer = KernelTimer(n)
+        for i in range(n):
+            timer.arm(i, "router")
+            moe.router_logits(x, wrs[i % copies], logits)
+        torch.cuda.synchronize()
+        ms = timer.times_ms()
+        timer.close()
+        us = 1e3 * sum(ms) / len(ms)
+        nbytes = E * H * 2 + w.T * H * 2 + w.T * E * 4
+        flops = 2.0 * w.T * E * H
+        res[name] = {"T": w.T, "mean_us": us, "gbs": nbytes / (us * 1e-6) / 1e9, "tflops": flops / (us * 1e-6) / 1e12,
+                     "kernel": "router_gemv_kernel" if w.T < 64 else "router_mfma_kernel"}
+    res["decode"]["hbm_frac"] = res["decode"]["gbs"] / HBM_PEAK_GBS
+    res["prefill"]["mfma_frac"] = res["prefill"]["tflops"] / BF16_PEAK_TFLOPS
+    res["workload"] = "router projection, E=512, H=2048, bf16 weights and activations, fp32 logits"
+    return res
+
+
 # ---- stacks of layers (decode steps through many layers) ------------------------------------
 
 def _placed_stack(torch, synth, w, dev, nthreads):
@@ -735,6 +779,7 @@ def main():
 
     res, data = decode_bench(args, torch, moe, synth, oracle)
     pre = None if args.no_prefill else prefill_bench(args, torch, moe, synth, oracle)
+    rtr = None if args.no_prefill else router_bench(args, torch, moe, synth, oracle)
     cpu = None if args.no_cpu else cpu_baseline(args, oracle, data)
     out = {
         "metric": METRIC,
@@ -760,6 +805,7 @@ def main():
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "prefill": pre,
+        "router": rtr,
     }
     print(json.dumps(out), flush=True)
 

@@ -324,7 +324,7 @@ moe_status moe_combine(const void* y, moe_dtype y_t, const float* w, int T, int 
 }
 
 moe_status moe_profile_next_launch(moe_kernel kernel, hipEvent_t start, hipEvent_t stop) {
-  if ((int)kernel < 0 || (int)kernel > (int)MOE_KERNEL_DECODE_PREP) return fail(MOE_EINVAL, "moe_profile_next_launch: kernel");
+  if ((int)kernel < 0 || (int)kernel > (int)MOE_KERNEL_ROUTER) return fail(MOE_EINVAL, "moe_profile_next_launch: kernel");
   if (!start || !stop) return fail(MOE_EINVAL, "moe_profile_next_launch: null event");
   ProfileReq& p = profile_req();
   p.kernel = (int)kernel;

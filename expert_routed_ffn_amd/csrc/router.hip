@@ -51,27 +51,38 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   float acc[kGemvT];
 #pragma unroll
   for (int t = 0; t < kGemvT; ++t) acc[t] = 0.0f;
-  for (int c = lane * 8; c < H; c += 512) {
-    const uint4 wv = *reinterpret_cast<const uint4*>(row + c);
-    const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
-                         bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+  // Four 1 KB steps of the row per pass, their loads issued before any use.
+  for (int c0 = lane * 8; c0 < H; c0 += 4 * 512) {
+    uint4 wv[4];
 #pragma unroll
-    for (int t = 0; t < kGemvT; ++t) {
-      if (t >= nt) break;
-      float xf[8];
-      const size_t xi = (size_t)(t0 + t) * H + c;
-      if constexpr (XF32) {
-        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + xi);
-        const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + xi + 4);
-        xf[0] = a.x; xf[1] = a.y; xf[2] = a.z; xf[3] = a.w;
-        xf[4] = b.x; xf[5] = b.y; xf[6] = b.z; xf[7] = b.w;
-      } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + xi);
-        xf[0] = bf16_lo(v.x); xf[1] = bf16_hi(v.x); xf[2] = bf16_lo(v.y); xf[3] = bf16_hi(v.y);
-        xf[4] = bf16_lo(v.z); xf[5] = bf16_hi(v.z); xf[6] = bf16_lo(v.w); xf[7] = bf16_hi(v.w);
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 512 * u;
+      wv[u] = c < H ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 512 * u;
+      if (c >= H) break;
+      const float wf[8] = {bf16_lo(wv[u].x), bf16_hi(wv[u].x), bf16_lo(wv[u].y), bf16_hi(wv[u].y),
+                           bf16_lo(wv[u].z), bf16_hi(wv[u].z), bf16_lo(wv[u].w), bf16_hi(wv[u].w)};
+#pragma unroll
+      for (int t = 0; t < kGemvT; ++t) {
+        if (t >= nt) break;
+        float xf[8];
+        const size_t xi = (size_t)(t0 + t) * H + c;
+        if constexpr (XF32) {
+          const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + xi);
+          const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + xi + 4);
+          xf[0] = a.x; xf[1] = a.y; xf[2] = a.z; xf[3] = a.w;
+          xf[4] = b.x; xf[5] = b.y; xf[6] = b.z; xf[7] = b.w;
+        } else {
+          const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + xi);
+          xf[0] = bf16_lo(v.x); xf[1] = bf16_hi(v.x); xf[2] = bf16_lo(v.y); xf[3] = bf16_hi(v.y);
+          xf[4] = bf16_lo(v.z); xf[5] = bf16_hi(v.z); xf[6] = bf16_lo(v.w); xf[7] = bf16_hi(v.w);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t] = __builtin_fmaf(xf[j], wf[j], acc[t]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[t] = __builtin_fmaf(xf[j], wf[j], acc[t]);
     }
   }
 #pragma unroll
