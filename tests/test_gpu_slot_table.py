@@ -270,5 +270,15 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, n_slots):
     assert fused.stats() == split.stats()
     assert np.array_equal(fused.map_host(), split.map_host())
     assert fused.stats()["misses"] > 0
+    # every filled slot holds its expert's master blob: the gate and up planes
+    # written by the read-through items, the rest by the side-stream copy
+    smap = fused.map_host().reshape(-1)
+    slots_h = fused.slots.cpu().numpy()
+    host_h = host.numpy()
+    filled = np.flatnonzero(smap >= 0)
+    assert len(filled) == n_slots
+    for g in filled:
+        sl = int(smap[g])
+        assert np.array_equal(slots_h[sl * eb:(sl + 1) * eb], host_h[g * eb:(g + 1) * eb]), (g, sl)
     for t in tables:
         t.close()
