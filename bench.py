@@ -251,11 +251,11 @@ def decode_bench(args, torch, moe, synth, oracle):
     return res, (x_np, lg_np, ex, w)
 
 
-def prefill_bench(args, torch, moe, synth, oracle):
+def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2):
     """8,192-token prompt chunk through one layer (MFMA path)."""
     import numpy as np
 
-    w = synth.prefill(args.prefill_bias)
+    w = synth.prefill(args.prefill_bias, bits)
     dev = torch.device("cuda:0")
     ex = w.experts(nthreads=synth.default_threads())
     x_np, lg_np = w.x(), w.logits()
@@ -309,7 +309,7 @@ def prefill_bench(args, torch, moe, synth, oracle):
     dn_flops = 2.0 * n * w.I * w.H
     counts = np.bincount(bufs["ids"].cpu().numpy().reshape(-1), minlength=w.E)
     return {
-        "workload": f"prefill chunk: T=8192, 512 experts, top-10, hidden 2048, intermediate 512, 2-bit, "
+        "workload": f"prefill chunk: T=8192, 512 experts, top-10, hidden 2048, intermediate 512, {bits}-bit, "
                     f"Zipf({1.1 * args.prefill_bias:g}) router bias",
         "value": T / el,
         "unit": "tokens/s",
@@ -324,7 +324,7 @@ def prefill_bench(args, torch, moe, synth, oracle):
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "traffic": measured_traffic("mfma_gateup"),
+            "traffic": measured_traffic("mfma_gateup") if bits == 2 else None,
             "kernel": "mfma_ffn_kernel gate/up (fp16 MFMA, weights decoded in LDS)",
             "flops_per_launch": gu_flops,
             "mean_us": gu_ms * 1e3,
@@ -376,6 +376,11 @@ def router_bench(args, torch, moe, synth, oracle):
     res["prefill"]["mfma_frac"] = res["prefill"]["tflops"] / BF16_PEAK_TFLOPS
     res["workload"] = "router projection, E=512, H=2048, bf16 weights and activations, fp32 logits"
     return res
+
+
+def prefill4_bench(args, torch, moe, synth, oracle):
+    """The prefill chunk with 4-bit weights (same routing and shapes)."""
+    return {"metric": "MoE-layer prefill tokens/s, 4-bit weights", **prefill_bench(args, torch, moe, synth, oracle, 4)}
 
 
 # ---- stacks of layers (decode steps through many layers) ------------------------------------
@@ -739,10 +744,11 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-bias", type=float, default=1.0, help="scale of the Zipf(1.1) router bias")
-    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep", "crossover"], default="layer",
+    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep", "crossover", "prefill4"], default="layer",
                     help="layer: the decode/verify layer (+ prefill), the default; stack125b / sweep: decode "
                          "steps through a 48- or 40-layer stack; crossover: layer step time against T for the "
-                         "GEMV and MFMA paths; the last three print their own JSON line")
+                         "GEMV and MFMA paths; prefill4: the prefill chunk with 4-bit weights; all but layer print "
+                         "their own JSON line")
     ap.add_argument("--stack-steps", type=int, default=0, help="steps of a stack run (default 256 / 64)")
     ap.add_argument("--stack-chunk", type=int, default=16, help="steps per captured graph in stack runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -773,7 +779,8 @@ def main():
         del src, dst
 
     if args.workload != "layer":
-        fn = {"stack125b": stack125b_bench, "sweep": sweep_bench, "crossover": crossover_bench}[args.workload]
+        fn = {"stack125b": stack125b_bench, "sweep": sweep_bench, "crossover": crossover_bench,
+              "prefill4": prefill4_bench}[args.workload]
         print(json.dumps({**fn(args, torch, moe, synth, oracle), "n_gpus": 1}), flush=True)
         return
 

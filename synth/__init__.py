@@ -254,10 +254,11 @@ def stack125b() -> Workload:
                     extra={"steps": 256, "drift_sigma": 0.05, "slots": 4096})
 
 
-def prefill(bias_scale: float = 1.0) -> Workload:
-    """8,192 tokens, 512 experts, top-10, hidden 2048, intermediate 512, 2-bit, Zipf(1.1 * bias_scale)."""
-    return Workload("prefill" if bias_scale == 1.0 else f"prefill_l{bias_scale:g}", E=512, k=10, H=2048, I=512,
-                    T=8192, bits=2, x_dtype="bf16", zipf_s=1.1 * bias_scale)
+def prefill(bias_scale: float = 1.0, bits: int = 2) -> Workload:
+    """8,192 tokens, 512 experts, top-10, hidden 2048, intermediate 512, 2-bit (or `bits`), Zipf(1.1 * bias_scale)."""
+    name = "prefill" if bias_scale == 1.0 else f"prefill_l{bias_scale:g}"
+    return Workload(name if bits == 2 else f"{name}_b{bits}", E=512, k=10, H=2048, I=512, T=8192, bits=bits,
+                    x_dtype="bf16", zipf_s=1.1 * bias_scale)
 
 
 def drifted_bias(w: Workload, layer: int, step: int, sigma: float) -> np.ndarray:
