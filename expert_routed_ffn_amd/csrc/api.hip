@@ -65,7 +65,7 @@ moe_status check_ek(const char* fn, int E, int k) {
 }
 
 moe_status check_shape(const char* fn, int H, int I, int bits) {
-  if (bits != 2 && bits != 4) return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": bits=%lld (2 or 4)", bits));
+  if (bits < 2 || bits > 4) return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": bits=%lld (2, 3 or 4)", bits));
   if (H < 32 || H > 16384 || H % 32)
     return fail(MOE_EUNSUPPORTED, std::string(fn) + fmt(": H=%lld (multiple of 32 in [32, 16384])", H));
   if (I < 32 || I > 8192 || I % 32)

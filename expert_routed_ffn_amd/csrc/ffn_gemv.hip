@@ -136,9 +136,21 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 // sum over the chunk of (128 + q_c) * x_c for the BITS-bit codes in `code`.
 template <int BITS, bool SPLIT>
 __device__ __forceinline__ float chunk_dot(const uint32_t (&code)[BITS], const XChunk<SPLIT>& x) {
+  float acc = 0.f;
+  if constexpr (BITS == 3) {
+    // words 0-1: the low two bits of the pairs as in the 2-bit layout; word 2:
+    // the high bit of column pair P at bits P and 16 + P
+#pragma unroll
+    for (int P = 0; P < 16; ++P) {
+      const uint32_t hi = (code[2] >> P) & 0x00010001u;
+      const uint32_t v = and_or(code[P / 8] >> (2 * (P % 8)), 0x00030003u, 0x43004300u) | (hi << 2);
+      acc = dot2(v, x.hi[P], acc);
+      if constexpr (SPLIT) acc = dot2(v, x.lo[P], acc);
+    }
+    return acc;
+  }
   constexpr uint32_t kMask = BITS == 2 ? 0x00030003u : 0x000F000Fu;
   constexpr int kPairs = 16 / BITS;  // code pairs per word
-  float acc = 0.f;
 #pragma unroll
   for (int d = 0; d < BITS; ++d)
 #pragma unroll
@@ -156,6 +168,10 @@ __device__ __forceinline__ void load_codes(uint32_t (&code)[BITS], const uint8_t
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     code[0] = v.x;
     code[1] = v.y;
+  } else if constexpr (BITS == 3) {  // 12-byte chunks: 4-byte aligned only
+    code[0] = reinterpret_cast<const uint32_t*>(p)[0];
+    code[1] = reinterpret_cast<const uint32_t*>(p)[1];
+    code[2] = reinterpret_cast<const uint32_t*>(p)[2];
   } else {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     code[0] = v.x;
@@ -916,7 +932,7 @@ struct RouteOut {
 #define MOE_ROUTED_NI4 4
 #endif
 template <int BITS, bool SPLIT>
-constexpr int kRoutedNI = BITS == 4 ? (SPLIT ? 2 : MOE_ROUTED_NI4) : (SPLIT ? MOE_ROUTED_NI_SPLIT : MOE_ROUTED_NI);
+constexpr int kRoutedNI = BITS >= 3 ? (SPLIT ? 2 : MOE_ROUTED_NI4) : (SPLIT ? MOE_ROUTED_NI_SPLIT : MOE_ROUTED_NI);
 
 // Workgroup 0 writes the routing and dispatch outputs (the down kernel and the
 // caller read them after the launch); every other workgroup routes in LDS,
@@ -950,8 +966,9 @@ moe_status launch_wide_routed(DecodeArgs& a, const RouteOut& r, int max_active, 
 
 template <bool SPLIT, bool YBF16, int EPL>
 moe_status launch_routed_b(DecodeArgs& a, const RouteOut& r, int bits, int max_active, hipStream_t s) {
-  return bits == 2 ? launch_wide_routed<2, SPLIT, YBF16, EPL>(a, r, max_active, s)
-                   : launch_wide_routed<4, SPLIT, YBF16, EPL>(a, r, max_active, s);
+  return bits == 2   ? launch_wide_routed<2, SPLIT, YBF16, EPL>(a, r, max_active, s)
+         : bits == 3 ? launch_wide_routed<3, SPLIT, YBF16, EPL>(a, r, max_active, s)
+                     : launch_wide_routed<4, SPLIT, YBF16, EPL>(a, r, max_active, s);
 }
 
 template <int BITS, int TM, bool SPLIT, bool YBF16>
@@ -979,7 +996,9 @@ moe_status launch_t(DecodeArgs& a, int T, int max_active, hipStream_t s) {
 
 template <bool SPLIT, bool YBF16>
 moe_status launch_b(DecodeArgs& a, int bits, int T, int max_active, hipStream_t s) {
-  return bits == 2 ? launch_t<2, SPLIT, YBF16>(a, T, max_active, s) : launch_t<4, SPLIT, YBF16>(a, T, max_active, s);
+  return bits == 2   ? launch_t<2, SPLIT, YBF16>(a, T, max_active, s)
+         : bits == 3 ? launch_t<3, SPLIT, YBF16>(a, T, max_active, s)
+                     : launch_t<4, SPLIT, YBF16>(a, T, max_active, s);
 }
 
 DecodeArgs make_args(const moe_qlayer& q, const void* x, int T, int k, const int32_t* sorted_assign,

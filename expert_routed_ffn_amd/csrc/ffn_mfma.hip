@@ -58,10 +58,6 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 32;
 constexpr int kXcd = 8;  // accelerator dies (each with its own L2) that workgroups are spread over
-#ifndef MOE_MFMA_PREFETCH
-#define MOE_MFMA_PREFETCH 2
-#endif
-constexpr int kPrefetch = MOE_MFMA_PREFETCH;  // K-steps of global loads in flight ahead of the MFMAs
 // LDS tile rows: 0 = 80-byte pitch (padded); 1, 2 = 64-byte pitch with the
 // four 16-byte chunks of a row permuted by chunk ^ ((row >> SHIFT) & 3),
 // SHIFT = 2 or 1.  Measured on gfx950 with 128-bit reads in the fragment
@@ -124,6 +120,18 @@ __device__ __forceinline__ void decode16_b4(uint32_t c0, uint32_t c1, uint32_t s
       const float qe = (float)(q2 & 0xFFu), qo = (float)(q2 >> 16);
       out[4 * w + p] = pack_f16(__builtin_fmaf(s, qe, m), __builtin_fmaf(s, qo, m));
     }
+  }
+}
+
+// BITS = 3: `lo` holds the low two bits of 16 codes (pair p at bits 2p /
+// 16+2p, as for 2 bits) and `hi` their high bits (pair p at bits p / 16+p).
+__device__ __forceinline__ void decode16_b3(uint32_t lo, uint32_t hi, uint32_t smw, uint32_t (&out)[8]) {
+  const float s = f16lo(smw), m = f16hi(smw);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t q2 = ((lo >> (2 * p)) & 0x00030003u) | (((hi >> p) & 0x00010001u) << 2);
+    const float qe = (float)(q2 & 0xFFu), qo = (float)(q2 >> 16);
+    out[p] = pack_f16(__builtin_fmaf(s, qe, m), __builtin_fmaf(s, qo, m));
   }
 }
 
@@ -329,14 +337,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
   // One K-step's global data, held in registers between its load and its LDS store.
   struct Stage {
     uint4 a[A_CHUNKS];
-    uint32_t code[B_HALVES][BITS / 2 == 1 ? 1 : 2];
+    uint32_t code[B_HALVES][BITS == 2 ? 1 : 2];
     uint32_t smw;
   };
 
   // Loads are unconditional (rows past the tile's end read a valid row whose
   // results are never stored), so every K-step issues the same loads and the
   // compiler can wait for one stage while later stages stay in flight.
-  auto load_stage = [&](Stage& st, int ks) {
+  auto load_stage = [&](int ks) {
+    Stage st;
 #pragma unroll
     for (int jj = 0; jj < A_CHUNKS; ++jj)
       st.a[jj] = *reinterpret_cast<const uint4*>(a_row[jj] + (int64_t)ks * kBK * 2 + a_col16[jj] * 16);
@@ -345,6 +354,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
       const int b_half = b_half0 + hh;
       if constexpr (BITS == 2) {
         st.code[hh][0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 8 + b_half * 4);
+      } else if constexpr (BITS == 3) {  // low bits of this half, then the block's high-bit word
+        st.code[hh][0] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 12 + b_half * 4);
+        st.code[hh][1] = *reinterpret_cast<const uint32_t*>(b_codes + (int64_t)ks * 12 + 8) >> (8 * b_half);
       } else {
         const uint2 v = *reinterpret_cast<const uint2*>(b_codes + (int64_t)ks * 16 + b_half * 8);
         st.code[hh][0] = v.x;
@@ -352,6 +364,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
       }
     }
     st.smw = *reinterpret_cast<const uint32_t*>(b_sm + (int64_t)ks * 4);
+    return st;
   };
 
   // A chunks of one K-step into LDS buffer `buf`.
@@ -364,18 +377,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
     }
   };
   // This thread's B slice of one K-step, decoded into LDS buffer `buf`.
-  auto store_b = [&](const uint32_t (&code)[B_HALVES][BITS / 2 == 1 ? 1 : 2], uint32_t smw, int buf) {
+  auto store_b = [&](const uint32_t (&code)[B_HALVES][BITS == 2 ? 1 : 2], uint32_t smw, int buf) {
 #pragma unroll
     for (int hh = 0; hh < B_HALVES; ++hh) {
       uint32_t w[8];  // rows past I (or H) decode a valid row; their columns are never stored
       if constexpr (BITS == 2) decode16_b2(code[hh][0], smw, w);
+      else if constexpr (BITS == 3) decode16_b3(code[hh][0], code[hh][1], smw, w);
       else decode16_b4(code[hh][0], code[hh][1], smw, w);
       const int c0 = 2 * (b_half0 + hh);
       *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0)]) = make_uint4(w[0], w[1], w[2], w[3]);
       *reinterpret_cast<uint4*>(&lds_b[buf][lds_off(b_r, c0 + 1)]) = make_uint4(w[4], w[5], w[6], w[7]);
     }
   };
-  auto store_stage = [&](const Stage& st, int buf) {
+  auto store_stage = [&](const Stage st, int buf) {
     store_a(st.a, buf);
     store_b(st.code, st.smw, buf);
   };
@@ -441,7 +455,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
         bp.sm = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bs_voff, ks * 4, 0));
       };
       auto store_bpair = [&](const BPair& bp, int e, int buf) {  // e: which K-step of the pair
-        uint32_t code[B_HALVES][BITS / 2 == 1 ? 1 : 2];
+        uint32_t code[B_HALVES][BITS == 2 ? 1 : 2];
         if constexpr (B_HALVES == 2) {
           if constexpr (BITS == 2) {
             code[0][0] = e ? bp.c[0].z : bp.c[0].x;
@@ -529,29 +543,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
       }
     }
   } else {
-    // Software pipeline: global loads run DEPTH K-steps ahead of the MFMAs
-    // (stage s sits in st[s % DEPTH] from its load until its LDS store); LDS is
-    // double-buffered, one barrier per K-step.  The loop is unrolled by DEPTH so
-    // the register stages are static, and it has no branch around a load or a
-    // store: stages past the end reload the last K-step (never used), so every
-    // iteration issues the same loads and a store waits only for its own stage.
-    constexpr int DEPTH = kPrefetch;
-    Stage st[DEPTH];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_stage(st[d], min(d, KS - 1));
-    store_stage(st[0], 0);
+    // Software pipeline: global loads run two K-steps ahead of the MFMAs
+    // (even stages in s0, odd in s1, from the load to the LDS store); LDS is
+    // double-buffered, one barrier per K-step.  No load sits behind a branch:
+    // stages past the end reload the last K-step (never used), so a store
+    // waits only for its own stage.
+    Stage s0 = load_stage(0), s1 = load_stage(min(1, KS - 1));
+    store_stage(s0, 0);
     __syncthreads();
-    for (int kb = 0; kb < KS; kb += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int ks = kb + d;
-        load_stage(st[d], min(ks + DEPTH, KS - 1));  // st[d] held stage ks, already in LDS
-        if (ks < KS) mma_stage(ks & 1);
-        store_stage(st[(d + 1) % DEPTH], (ks + 1) & 1);
-        __syncthreads();
-      }
+    for (int kb = 0; kb < KS; kb += 2) {
+      s0 = load_stage(min(kb + 2, KS - 1));  // s0 held stage kb, already in LDS
+      mma_stage(0);
+      store_stage(s1, 1);
+      __syncthreads();
+      s1 = load_stage(min(kb + 3, KS - 1));
+      if (kb + 1 < KS) mma_stage(1);
+      store_stage(s0, 0);
+      __syncthreads();
     }
   }
+
 
   // ---- epilogue.  The MFMAs take the weights as their first operand, so a
   // lane holds 4 consecutive output columns of one row: row 16 * fi + (lane & 15),
@@ -682,7 +693,7 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   const int tiles_pad = (int)ceil_div(max_tiles, kXcd) * kXcd;  // whole rounds over the dies
   // The pair kernel addresses x, h and an expert blob with 32-bit byte offsets.
   constexpr int64_t kOff = int64_t(1) << 31;
-  constexpr bool kPairOk = true;
+  constexpr bool kPairOk = BITS != 3;  // the pair loads assume 8- or 16-byte K-steps
   const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
   if (kPairOk && off_ok && q.H % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk, kNT>,
@@ -721,6 +732,9 @@ moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, in
   if (q.bits == 2)
     return yb ? launch_all<2, true>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s)
               : launch_all<2, false>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s);
+  if (q.bits == 3)
+    return yb ? launch_all<3, true>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s)
+              : launch_all<3, false>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s);
   return yb ? launch_all<4, true>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s)
             : launch_all<4, false>(q, L, x, xf, T, k, offsets, sorted_assign, active, n_active, y, w, s);
 }

@@ -17,13 +17,16 @@
  *   - 2-bit class weights (Q2_0) are the fast size: Strata feature, section
  *     "3. 바로 써먹기", speed table.
  *
- * Weight format (b = 2 or 4).  A matrix [R x K] (K % 32 == 0) is split into
- * blocks of 32 weights along K.  Each block carries an IEEE binary16 scale s
- * and min m; weight = s * q + m for the block's b-bit unsigned codes q.
- *   code plane: row r is K*b/32 little-endian uint32 words; word w holds
- *     columns w*(32/b) ... (w+1)*(32/b) - 1; column c of a word sits at bit
- *     16*(c % 2) + b*(c / 2), so even columns fill the low halfword and odd
- *     columns the high halfword;
+ * Weight format (b = 2, 3 or 4).  A matrix [R x K] (K % 32 == 0) is split
+ * into blocks of 32 weights along K.  Each block carries an IEEE binary16
+ * scale s and min m; weight = s * q + m for the block's b-bit unsigned codes q.
+ *   code plane: row r is K*b/32 little-endian uint32 words.  b = 2, 4: word w
+ *     holds columns w*(32/b) ... (w+1)*(32/b) - 1; column c of a word sits at
+ *     bit 16*(c % 2) + b*(c / 2), so even columns fill the low halfword and
+ *     odd columns the high halfword.  b = 3: three words per block; words 0
+ *     and 1 hold the low two bits of the block's codes exactly as the b = 2
+ *     layout holds codes, word 2 holds the high bit of block column j at bit
+ *     16*(j % 2) + j / 2 (q = low + 4 * high);
  *   s/m plane: row r is K/32 uint32 words, scale in bits 0-15, min in 16-31;
  *   expert blob: Wg codes, Wg s/m, Wu codes, Wu s/m, Wd codes, Wd s/m, each
  *     plane starting on a 256-byte boundary; Wg and Wu are [I x H], Wd is
@@ -41,7 +44,7 @@
  *     thread-local message for the last failing call on this thread.
  *   - A HIP runtime or launch failure is reported as MOE_EHIP.
  *   - Limits: 1 <= E <= 1024, 1 <= k <= min(16, E), H % 32 == 0 and
- *     I % 32 == 0 with 32 <= H <= 16384 and 32 <= I <= 8192, b in {2, 4},
+ *     I % 32 == 0 with 32 <= H <= 16384 and 32 <= I <= 8192, b in {2, 3, 4},
  *     T >= 0 (T == 0 enqueues nothing and returns MOE_OK).
  *   - Device buffers that the kernels read with 128-bit loads (expert blobs,
  *     activations) must be 16-byte aligned; the expert stride must be a

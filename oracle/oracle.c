@@ -98,12 +98,24 @@ static uint32_t read_u32_le(const uint8_t* p) {
  * s*q + m.  Exact in double: an fp16 times a code below 16 has at most 15
  * significant bits, and the sum with an fp16 spans far fewer than 53 bits. */
 static double weight_at(const uint8_t* codes, const uint8_t* sm, int K, int bits, int r, int c) {
-  int per_word = 32 / bits;
-  int64_t row_words = (int64_t)K / per_word;
-  uint32_t word = read_u32_le(codes + 4 * ((int64_t)r * row_words + c / per_word));
-  int cw = c % per_word;
-  int shift = 16 * (cw % 2) + bits * (cw / 2);
-  uint32_t q = (word >> shift) & ((1u << bits) - 1u);
+  int64_t row_words = (int64_t)K * bits / 32;
+  uint32_t q;
+  if (bits == 3) {
+    /* three words per 32-column block: the low two bits of the codes laid out
+     * as in the 2-bit format (16 columns per word), then one word of high bits,
+     * block column j at bit 16*(j%2) + j/2 */
+    const uint8_t* blk = codes + 4 * ((int64_t)r * row_words + 3 * (c / 32));
+    int j = c % 32, cw = j % 16;
+    uint32_t lo = (read_u32_le(blk + 4 * (j / 16)) >> (16 * (cw % 2) + 2 * (cw / 2))) & 3u;
+    uint32_t hi = (read_u32_le(blk + 8) >> (16 * (j % 2) + j / 2)) & 1u;
+    q = lo + 4u * hi;
+  } else {
+    int per_word = 32 / bits;
+    uint32_t word = read_u32_le(codes + 4 * ((int64_t)r * row_words + c / per_word));
+    int cw = c % per_word;
+    int shift = 16 * (cw % 2) + bits * (cw / 2);
+    q = (word >> shift) & ((1u << bits) - 1u);
+  }
   uint32_t smw = read_u32_le(sm + 4 * ((int64_t)r * (K / 32) + c / 32));
   double s = oracle_f16((uint16_t)(smw & 0xFFFF));
   double m = oracle_f16((uint16_t)(smw >> 16));
@@ -281,7 +293,7 @@ void oracle_router_logits(const void* x, int x_is_bf16, const uint16_t* wr, int 
 int oracle_layer(const void* x, int x_is_bf16, const float* logits, const uint8_t* experts, int64_t stride, int T,
                  int E, int k, int H, int I, int bits, const double* residual, int32_t* ids, double* w, double* y,
                  double* out) {
-  if (H % 32 || I % 32 || (bits != 2 && bits != 4)) return -1;
+  if (H % 32 || I % 32 || bits < 2 || bits > 4) return -1;
   if (oracle_route(logits, T, E, k, ids, w) != 0) return -1;
   size_t n = (size_t)H * (size_t)I;
   double* wg = (double*)malloc(sizeof(double) * n);

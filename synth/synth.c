@@ -186,13 +186,19 @@ void synth_blob_layout(int H, int I, int bits, int64_t* off) {
   off[6] = (int64_t)o;
 }
 
-/* Encode a [R x K] matrix of doubles into the code plane and the s/m plane. */
+/* Encode a [R x K] matrix of doubles into the code plane and the s/m plane.
+ * bits 2 and 4: word w of a row holds columns w*(32/bits) .., column c of the
+ * word at bit 16*(c%2) + bits*(c/2).  bits 3: three words per 32-column block;
+ * words 0 and 1 hold the low two bits of each code as the 2-bit layout does,
+ * word 2 the high bit, block column j at bit 16*(j%2) + j/2. */
 void synth_quantize_matrix(const double* w, int R, int K, int bits, uint32_t* codes, uint32_t* sm) {
-  const int qmax = (1 << bits) - 1, per_word = 32 / bits, nb = K / 32;
+  const int qmax = (1 << bits) - 1, nb = K / 32;
+  const int per_word = bits == 3 ? 16 : 32 / bits;
+  const size_t row_words = (size_t)K * (size_t)bits / 32;
   for (int r = 0; r < R; ++r) {
     const double* row = w + (size_t)r * K;
-    uint32_t* crow = codes + (size_t)r * (size_t)(K / per_word);
-    memset(crow, 0, sizeof(uint32_t) * (size_t)(K / per_word));
+    uint32_t* crow = codes + (size_t)r * row_words;
+    memset(crow, 0, sizeof(uint32_t) * row_words);
     for (int b = 0; b < nb; ++b) {
       const double* blk = row + 32 * b;
       double mn = blk[0], mx = blk[0];
@@ -206,8 +212,14 @@ void synth_quantize_matrix(const double* w, int R, int K, int bits, uint32_t* co
           double v = nearbyint((blk[j] - md) / sd); /* default rounding mode: ties to even */
           q = v < 0.0 ? 0 : (v > (double)qmax ? qmax : (int)v);
         }
-        int col = 32 * b + j, word = col / per_word, c = col % per_word;
-        crow[word] |= (uint32_t)q << (16 * (c & 1) + bits * (c >> 1));
+        if (bits == 3) {
+          const int c = j % 16;
+          crow[3 * b + j / 16] |= (uint32_t)(q & 3) << (16 * (c & 1) + 2 * (c >> 1));
+          crow[3 * b + 2] |= (uint32_t)(q >> 2) << (16 * (j & 1) + (j >> 1));
+        } else {
+          int col = 32 * b + j, word = col / per_word, c = col % per_word;
+          crow[word] |= (uint32_t)q << (16 * (c & 1) + bits * (c >> 1));
+        }
       }
     }
   }

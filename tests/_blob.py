@@ -5,8 +5,11 @@ tests can build experts whose decoded weights are known exactly:
 
 * a [R x K] matrix is split in blocks of 32 along K, each with an fp16 scale s
   and fp16 min m; the weight is s*q + m for a b-bit code q;
-* code plane: per row K*b/32 little-endian uint32 words; word w holds columns
-  w*(32/b) ..; column c of the word sits at bit 16*(c % 2) + b*(c // 2);
+* code plane: per row K*b/32 little-endian uint32 words.  b = 2, 4: word w
+  holds columns w*(32/b) ..; column c of the word sits at bit
+  16*(c % 2) + b*(c // 2).  b = 3: three words per 32-column block, the low two
+  bits of each code in words 0-1 as for b = 2, the high bit in word 2 at bit
+  16*(j % 2) + j // 2 for block column j;
 * s/m plane: per row K/32 uint32 words, scale in the low half, min in the high;
 * blob: Wg codes, Wg s/m, Wu codes, Wu s/m, Wd codes, Wd s/m, each plane on a
   256-byte boundary; Wg, Wu are [I x H], Wd is [H x I].
@@ -36,12 +39,18 @@ def f16_bits(x: float) -> int:
 def pack_matrix(q: np.ndarray, scale: np.ndarray, mn: np.ndarray, bits: int):
     """q: int [R,K] codes; scale, mn: float [R,K/32] (must be exact fp16 values)."""
     R, K = q.shape
-    per_word = 32 // bits
-    codes = np.zeros((R, K // per_word), np.uint32)
+    codes = np.zeros((R, K * bits // 32), np.uint32)
     for r in range(R):
         for col in range(K):
-            w, c = divmod(col, per_word)
-            codes[r, w] |= np.uint32(int(q[r, col]) << (16 * (c % 2) + bits * (c // 2)))
+            v = int(q[r, col])
+            if bits == 3:
+                blk, j = divmod(col, 32)
+                half, c = divmod(j, 16)
+                codes[r, 3 * blk + half] |= np.uint32((v & 3) << (16 * (c % 2) + 2 * (c // 2)))
+                codes[r, 3 * blk + 2] |= np.uint32((v >> 2) << (16 * (j % 2) + j // 2))
+            else:
+                w, c = divmod(col, 32 // bits)
+                codes[r, w] |= np.uint32(v << (16 * (c % 2) + bits * (c // 2)))
     sm = np.zeros((R, K // 32), np.uint32)
     for r in range(R):
         for b in range(K // 32):

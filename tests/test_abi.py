@@ -24,11 +24,13 @@ def test_abi_version_and_status_strings():
 
 
 def test_expert_bytes_formula():
-    for H, I, b in [(2048, 512, 2), (2048, 512, 4), (64, 32, 2), (96, 64, 4)]:
+    for H, I, b in [(2048, 512, 2), (2048, 512, 3), (2048, 512, 4), (64, 32, 2), (96, 64, 3), (96, 64, 4)]:
         assert m.expert_bytes(H, I, b) % 256 == 0
         assert m.expert_bytes(H, I, b) >= 3 * H * I * (b / 8 + 4 / 32)
     assert m.expert_bytes(2048, 512, 2) == 1179648
-    assert m.expert_bytes(2048, 512, 3) == 0  # unsupported width
+    assert m.expert_bytes(2048, 512, 3) == 1572864  # 3 * 2048 * 512 * (3/8 + 1/8)
+    assert m.expert_bytes(2048, 512, 5) == 0  # unsupported width
+    assert m.expert_bytes(2048, 512, 1) == 0
 
 
 NULL = None
@@ -77,7 +79,8 @@ def test_expert_ffn_argument_checks():
         return _st(L.moe_expert_ffn_q(ctypes.byref(q), x, x_t, T, k, fake, fake, fake, fake, fake, y_t, path, fake,
                                       ws_bytes, NULL))
 
-    assert call(_q(bits=3)) == _lib.MOE_EUNSUPPORTED
+    assert call(_q(bits=5)) == _lib.MOE_EUNSUPPORTED
+    assert call(_q(bits=1)) == _lib.MOE_EUNSUPPORTED
     assert call(_q(H=48)) == _lib.MOE_EUNSUPPORTED
     assert call(_q(I=16)) == _lib.MOE_EUNSUPPORTED
     assert call(_q(stride=100)) == _lib.MOE_EINVAL

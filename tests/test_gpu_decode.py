@@ -165,6 +165,9 @@ def _custom(E, k, H, I, T, bits, x_dtype="bf16", zipf=0.0, seed=3):
     (1024, 16, 64, 32, 5, 4, "bf16"),   # largest E and k
     (32, 3, 160, 96, 7, 2, "f32"),      # odd chunk counts, fp32 input
     (4, 1, 128, 64, 1, 4, "bf16"),
+    (64, 8, 2048, 512, 3, 3, "bf16"),   # 3-bit codes: wide kernels
+    (16, 4, 96, 64, 5, 3, "f32"),       # 3-bit codes: general kernels, fp32 input
+    (32, 3, 160, 96, 7, 3, "bf16"),
 ])
 def test_layer_gemv_shapes(moe, E, k, H, I, T, bits, x_dtype):
     w = _custom(E, k, H, I, T, bits, x_dtype)
@@ -304,6 +307,8 @@ def test_layer_decode_residual_bf16_outputs(moe, r_dtype, y_bf16):
     (1024, 16, 64, 32, 5, 4, "bf16"),
     (32, 3, 160, 96, 7, 2, "f32"),
     (8, 2, 256, 128, 12, 2, "bf16"),
+    (512, 10, 2048, 512, 3, 3, "bf16"),  # 3-bit codes through the routed gate/up launch
+    (48, 6, 96, 64, 4, 3, "f32"),
 ])
 def test_layer_decode_shapes(moe, E, k, H, I, T, bits, x_dtype):
     w = _custom(E, k, H, I, T, bits, x_dtype)

@@ -82,6 +82,8 @@ def _custom(E, k, H, I, T, bits, x_dtype="bf16", zipf=0.0, seed=5):
     (16, 4, 256, 96, 257, 4, "bf16", 1.0),  # I not a multiple of 64: partial N-tiles
     (32, 8, 160, 64, 200, 2, "f32", 1.2),   # K = 160: five K-steps, fp32 input
     (4, 1, 128, 64, 129, 4, "f32", 0.0),    # k = 1, one row past a tile
+    (16, 4, 256, 128, 300, 3, "bf16", 0.5), # 3-bit codes (the per-K-step loop)
+    (8, 2, 160, 96, 130, 3, "f32", 1.0),    # 3-bit, K = 160 and 96
 ])
 def test_mfma_small_cases_full(moe, E, k, H, I, T, bits, x_dtype, zipf):
     w = _custom(E, k, H, I, T, bits, x_dtype, zipf)

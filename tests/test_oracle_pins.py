@@ -74,7 +74,7 @@ def test_oracle_layout_matches_hand_layout():
 
 # ---- dequantization ---------------------------------------------------------------
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_every_code_position_decodes_to_its_own_column(bits):
     """A single nonzero code, swept over every column of a row, must decode at that column only."""
     H, I = 64, 32
@@ -95,7 +95,7 @@ def test_every_code_position_decodes_to_its_own_column(bits):
             assert np.array_equal(W, expect), (mat, c)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_scale_and_min_take_their_roles(bits):
     """W = s*q + m with s in the low half and m in the high half of the s/m word."""
     H, I = 64, 32
@@ -108,7 +108,7 @@ def test_scale_and_min_take_their_roles(bits):
             assert np.all(W == s * q + m)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_exactly_representable_blocks_round_trip(bits):
     """Blocks whose values are s*q + m with q spanning 0..qmax encode and decode exactly."""
     rng = np.random.default_rng(1)
@@ -131,7 +131,7 @@ def test_exactly_representable_blocks_round_trip(bits):
     assert np.array_equal(W, w)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_quantize_then_decode_error_within_half_step(bits):
     """|w - deq(quant(w))| <= s/2 plus the fp16 rounding of s and m."""
     qmax = (1 << bits) - 1
@@ -243,14 +243,14 @@ def _silu(z):
     return z / (1.0 + math.exp(-z))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_zero_input_gives_exactly_zero(bits):
     blob = synth.expert(0, 0, 1, 64, 32, bits, 0.02)
     h, y = oracle.expert_ffn(blob, 64, 32, bits, np.zeros(64))
     assert np.all(h == 0.0) and np.all(y == 0.0)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_constant_weight_expert_closed_form(bits):
     H, I = 96, 64
     (qg, sg, mg), (qu, su, mu), (qd, sd, md) = (1, 0.0625, -0.03125), (2, 0.03125, 0.015625), (1, 0.015625, -0.0625)
@@ -265,7 +265,7 @@ def test_constant_weight_expert_closed_form(bits):
     assert np.allclose(y, cd * I * h_ref, rtol=1e-13, atol=0)
 
 
-@pytest.mark.parametrize("bits,with_min", [(2, False), (2, True), (4, False), (4, True)])
+@pytest.mark.parametrize("bits,with_min", [(2, False), (2, True), (3, False), (3, True), (4, False), (4, True)])
 def test_identity_like_expert_closed_form(bits, with_min):
     """Wg, Wu pick one input column per row, Wd one h entry per output:
     y[n] = c * silu(a * x[pg[s[n]]]) * b * x[pu[s[n]]]."""
