@@ -120,10 +120,10 @@ class KernelTimer:
             self.hip.hipEventDestroy(b)
 
 
-def decode_bench(args, torch, moe, synth, oracle):
+def decode_bench(args, torch, moe, synth, oracle, bits: int = 2):
     import numpy as np
 
-    w = synth.decode_verify()
+    w = synth.decode_verify(bits)
     dev = torch.device("cuda:0")
     eb = w.expert_bytes
     t0 = time.time()
@@ -236,7 +236,7 @@ def decode_bench(args, torch, moe, synth, oracle):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": measured_traffic("gemv_gateup"),
+            "traffic": measured_traffic("gemv_gateup") if bits == 2 else None,
             "kernel": "ffn_route_gateup_kernel (routing + expert gate/up dequant-GEMV + SwiGLU)",
             "bytes_per_launch": gu_bytes,
             "mean_us": gu_ms * 1e3,
@@ -376,6 +376,17 @@ def router_bench(args, torch, moe, synth, oracle):
     res["prefill"]["mfma_frac"] = res["prefill"]["tflops"] / BF16_PEAK_TFLOPS
     res["workload"] = "router projection, E=512, H=2048, bf16 weights and activations, fp32 logits"
     return res
+
+
+def bits3_bench(args, torch, moe, synth, oracle):
+    """The decode/verify layer and the prefill chunk with 3-bit weights (same routing and shapes)."""
+    res, _ = decode_bench(args, torch, moe, synth, oracle, 3)
+    pre = None if args.no_prefill else prefill_bench(args, torch, moe, synth, oracle, 3)
+    return {"metric": "MoE-layer tokens/s, 3-bit weights", "unit": "tokens/s",
+            "decode": {"workload": "decode/verify layer, T=3, 512 experts, top-10, 2048 x 512, 3-bit",
+                       "value": res["value"], "ms_per_step": res["ms_per_step"], "unique_experts_per_step": res["U"],
+                       "layer_hbm_frac": res["layer_hbm_frac"], "roofline": res["roofline"]},
+            "prefill": pre}
 
 
 def prefill4_bench(args, torch, moe, synth, oracle):
@@ -744,10 +755,12 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-bias", type=float, default=1.0, help="scale of the Zipf(1.1) router bias")
-    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep", "crossover", "prefill4"], default="layer",
+    ap.add_argument("--workload", choices=["layer", "stack125b", "sweep", "crossover", "prefill4", "bits3"],
+                    default="layer",
                     help="layer: the decode/verify layer (+ prefill), the default; stack125b / sweep: decode "
                          "steps through a 48- or 40-layer stack; crossover: layer step time against T for the "
-                         "GEMV and MFMA paths; prefill4: the prefill chunk with 4-bit weights; all but layer print "
+                         "GEMV and MFMA paths; prefill4: the prefill chunk with 4-bit weights; bits3: decode layer "
+                         "and prefill chunk with 3-bit weights; all but layer print "
                          "their own JSON line")
     ap.add_argument("--stack-steps", type=int, default=0, help="steps of a stack run (default 256 / 64)")
     ap.add_argument("--stack-chunk", type=int, default=16, help="steps per captured graph in stack runs")
@@ -780,7 +793,7 @@ def main():
 
     if args.workload != "layer":
         fn = {"stack125b": stack125b_bench, "sweep": sweep_bench, "crossover": crossover_bench,
-              "prefill4": prefill4_bench}[args.workload]
+              "prefill4": prefill4_bench, "bits3": bits3_bench}[args.workload]
         print(json.dumps({**fn(args, torch, moe, synth, oracle), "n_gpus": 1}), flush=True)
         return
 

@@ -237,9 +237,10 @@ def tiny() -> Workload:
     return Workload("tiny", E=8, k=2, H=64, I=32, T=4, bits=2, x_dtype="f32")
 
 
-def decode_verify() -> Workload:
-    """512 experts, top-10, hidden 2048, intermediate 512, T=3 (1 token + 2 drafts), 2-bit, Zipf(1.1)."""
-    return Workload("decode_verify", E=512, k=10, H=2048, I=512, T=3, bits=2, x_dtype="bf16", zipf_s=1.1)
+def decode_verify(bits: int = 2) -> Workload:
+    """512 experts, top-10, hidden 2048, intermediate 512, T=3 (1 token + 2 drafts), 2-bit (or `bits`), Zipf(1.1)."""
+    return Workload("decode_verify" if bits == 2 else f"decode_verify_b{bits}", E=512, k=10, H=2048, I=512, T=3,
+                    bits=bits, x_dtype="bf16", zipf_s=1.1)
 
 
 def decode_sweep(T: int) -> Workload:
