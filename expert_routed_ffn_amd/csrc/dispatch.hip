@@ -78,11 +78,21 @@ __global__ __launch_bounds__(kBlock) void dispatch_scan_kernel(int nchunks, int 
   __shared__ int scan_sh[2 * kDispWaves];
   const int tid = threadIdx.x;
   if (tid < E) {
+    // exclusive scan of this expert's per-chunk counts, 16 chunks per batch:
+    // a batch's loads are issued before its stores, so they overlap instead of
+    // waiting one L2 round trip each behind the previous store
+    constexpr int kBatch = 16;
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_count[(size_t)c * E + tid];
-      chunk_count[(size_t)c * E + tid] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = c0 + u < nchunks ? chunk_count[(size_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (c0 + u < nchunks) {
+          chunk_count[(size_t)(c0 + u) * E + tid] = run;
+          run += v[u];
+        }
     }
     cnt[tid] = run;
   }

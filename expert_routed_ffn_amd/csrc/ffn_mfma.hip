@@ -224,9 +224,6 @@ struct GemmArgs {
 
 // Two waves per SIMD (two workgroups per CU): the compiler keeps the 64 x 128
 // accumulator tile of a wave in VGPRs within that budget.
-#ifndef MOE_MFMA_INTERLEAVE
-#define MOE_MFMA_INTERLEAVE 0
-#endif
 #ifndef MOE_MFMA_WAVES_PER_EU
 #define MOE_MFMA_WAVES_PER_EU 2
 #endif
@@ -479,23 +476,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
         }
         store_b(code, e ? bp.sm.y : bp.sm.x, buf);
       };
-      // MOE_MFMA_INTERLEAVE = V > 0: the decode of the next stage is spread over
-      // the MFMAs (one MFMA, then V VALU ops, 32 times), LDS writes last;
-      // 0: a fence after the MFMAs keeps the decode behind them.
-      auto mfma_fence = [] {
-        if constexpr (MOE_MFMA_INTERLEAVE == 0) __builtin_amdgcn_sched_barrier(0);
-      };
-      auto step_hint = [] {
-        if constexpr (MOE_MFMA_INTERLEAVE > 0) {
-          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);  // fragment reads
-#pragma unroll
-          for (int i = 0; i < FM * FN; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, MOE_MFMA_INTERLEAVE, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // LDS writes
-        }
-      };
       uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
       BPair bp0, bp1;
       load_a(sa0, 0);
@@ -508,36 +488,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
       for (int kb = 0; kb < KS; kb += 4) {
         load_a(sa0, min(kb + 2, KS - 1));
         mma_stage(0);  // stage kb
-        mfma_fence();
+        __builtin_amdgcn_sched_barrier(0);  // the decode below starts after the MFMAs are issued
         store_a(sa1, 1);
         store_bpair(bp0, 1, 1);
-        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
         load_a(sa1, min(kb + 3, KS - 1));
         load_bpair(bp0, min(kb + 4, KS - 2));
         mma_stage(1);  // stage kb + 1
-        mfma_fence();
+        __builtin_amdgcn_sched_barrier(0);  // the decode below starts after the MFMAs are issued
         store_a(sa0, 0);
         store_bpair(bp1, 0, 0);
-        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
         load_a(sa0, min(kb + 4, KS - 1));
         mma_stage(0);  // stage kb + 2
-        mfma_fence();
+        __builtin_amdgcn_sched_barrier(0);  // the decode below starts after the MFMAs are issued
         store_a(sa1, 1);
         store_bpair(bp1, 1, 1);
-        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
         load_a(sa1, min(kb + 5, KS - 1));
         load_bpair(bp1, min(kb + 6, KS - 2));
         mma_stage(1);  // stage kb + 3
-        mfma_fence();
+        __builtin_amdgcn_sched_barrier(0);  // the decode below starts after the MFMAs are issued
         store_a(sa0, 0);
         store_bpair(bp0, 0, 0);
-        step_hint();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
       }
