@@ -224,6 +224,10 @@ struct GemmArgs {
 
 // Two waves per SIMD (two workgroups per CU): the compiler keeps the 64 x 128
 // accumulator tile of a wave in VGPRs within that budget.
+// Activation rows loaded two K-steps at a time in the pair pipeline.
+#ifndef MOE_MFMA_APAIR
+#define MOE_MFMA_APAIR 1
+#endif
 #ifndef MOE_MFMA_WAVES_PER_EU
 #define MOE_MFMA_WAVES_PER_EU 2
 #endif
@@ -476,6 +480,55 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
         }
         store_b(code, e ? bp.sm.y : bp.sm.x, buf);
       };
+#if MOE_MFMA_APAIR
+      // A in pairs as well: a00/a01 hold stages 4j, 4j+1 and a10/a11 stages
+      // 4j+2, 4j+3; both K-steps of a pair are loaded back to back, so the
+      // second 64-byte half of each activation line is requested while the
+      // first is still in flight.
+      uint4 a00[A_CHUNKS], a01[A_CHUNKS], a10[A_CHUNKS], a11[A_CHUNKS];
+      BPair bp0, bp1;
+      load_a(a00, 0);
+      load_a(a01, 1);
+      load_a(a10, 2);
+      load_a(a11, 3);
+      load_bpair(bp0, 0);
+      load_bpair(bp1, 2);
+      store_a(a00, 0);
+      store_bpair(bp0, 0, 0);
+      __syncthreads();
+      for (int kb = 0; kb < KS; kb += 4) {
+        mma_stage(0);  // stage kb
+        __builtin_amdgcn_sched_barrier(0);  // the decode below starts after the MFMAs are issued
+        store_a(a01, 1);
+        store_bpair(bp0, 1, 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
+        load_a(a00, min(kb + 4, KS - 1));
+        load_a(a01, min(kb + 5, KS - 1));
+        load_bpair(bp0, min(kb + 4, KS - 2));
+        mma_stage(1);  // stage kb + 1
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(a10, 0);
+        store_bpair(bp1, 0, 0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage(0);  // stage kb + 2
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(a11, 1);
+        store_bpair(bp1, 1, 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(a10, min(kb + 6, KS - 1));
+        load_a(a11, min(kb + 7, KS - 1));
+        load_bpair(bp1, min(kb + 6, KS - 2));
+        mma_stage(1);  // stage kb + 3
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(a00, 0);
+        store_bpair(bp0, 0, 0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#else
       uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
       BPair bp0, bp1;
       load_a(sa0, 0);
@@ -517,6 +570,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);  // keep each K-step's loads and MFMAs in their own step
       }
+#endif
     }
   } else {
     // Software pipeline: global loads run two K-steps ahead of the MFMAs
