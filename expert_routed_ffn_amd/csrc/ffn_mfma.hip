@@ -12,7 +12,8 @@
 // fed to v_mfma_f32_16x16x32_f16 with fp32 accumulation.  One MFMA's K = 32 is
 // one quantization block, so every K-step decodes one block per weight row.
 //
-// Rounding points: decoded weight = fp16_rne(fp32 fma(s, q, m)); x is
+// Rounding points: decoded weight = fp16_rne(fp32 fma(s, q, m)) for 2-bit
+// codes and fp16_rne(s * q + m) (one fused fp16 operation) for 3- and 4-bit; x is
 // converted to fp16 once by a pre-pass (values beyond the fp16 range saturate
 // to +-65504); h = silu(g) * u is rounded to fp16 (saturating); products
 // accumulate in fp32.  The operands are fp16 rather than bf16 because the
@@ -41,8 +42,8 @@
 //
 // 2-bit decode uses a 4-entry fp16 table per (row, block): the packed pair of
 // codes (c_even, c_odd) in the two halfwords becomes a v_perm_b32 byte selector
-// (2c, 2c+1 per halfword), i.e. ~2 VALU ops per weight; 4-bit decodes with
-// fp32 fma per weight.
+// (2c, 2c+1 per halfword), i.e. ~2 VALU ops per weight; 4- and 3-bit codes
+// decode in packed fp16 (see below), about 2.5 VALU ops per weight.
 //
 // A small prep kernel turns (n_active, active, offsets) into the list of
 // (expert slot, first row) M-tiles; the GEMM grid is sized for the worst case
@@ -108,30 +109,49 @@ __device__ __forceinline__ void decode16_b2(uint32_t code, uint32_t smw, uint32_
   }
 }
 
+// 4- and 3-bit decode in packed fp16: a code pair (q_even, q_odd) or-ed into
+// 0x6400 per halfword is the fp16 pair (1024 + q); subtracting 1024 is exact,
+// and one fused multiply-add per pair gives fp16(s * q + m) with a single
+// rounding.  About 5 VALU ops per pair against 10 through fp32.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+struct Dec16 {  // the block's scale and min in both halfwords, and the -1024 pair
+  f16x2_t s2, m2, off;
+};
+__device__ __forceinline__ Dec16 dec16(uint32_t smw) {
+  Dec16 d;
+  d.s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(smw, smw, 0x01000100u));
+  d.m2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(smw, smw, 0x03020302u));
+  d.off = f16x2_t{(_Float16)-1024.0f, (_Float16)-1024.0f};
+  return d;
+}
+__device__ __forceinline__ uint32_t dec_pair(uint32_t magic_pair, const Dec16& d) {
+  const f16x2_t q = __builtin_bit_cast(f16x2_t, magic_pair) + d.off;
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d.s2, d.m2));
+}
+
 // BITS = 4: two words, 8 codes each (pair p at bits 4p / 16+4p).
 __device__ __forceinline__ void decode16_b4(uint32_t c0, uint32_t c1, uint32_t smw, uint32_t (&out)[8]) {
-  const float s = f16lo(smw), m = f16hi(smw);
+  const Dec16 d = dec16(smw);
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
     const uint32_t c = w ? c1 : c0;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t q2 = (c >> (4 * p)) & 0x000F000Fu;
-      const float qe = (float)(q2 & 0xFFu), qo = (float)(q2 >> 16);
-      out[4 * w + p] = pack_f16(__builtin_fmaf(s, qe, m), __builtin_fmaf(s, qo, m));
-    }
+    for (int p = 0; p < 4; ++p) out[4 * w + p] = dec_pair(and_or(c >> (4 * p), 0x000F000Fu, 0x64006400u), d);
   }
 }
 
 // BITS = 3: `lo` holds the low two bits of 16 codes (pair p at bits 2p /
 // 16+2p, as for 2 bits) and `hi` their high bits (pair p at bits p / 16+p).
 __device__ __forceinline__ void decode16_b3(uint32_t lo, uint32_t hi, uint32_t smw, uint32_t (&out)[8]) {
-  const float s = f16lo(smw), m = f16hi(smw);
+  const Dec16 d = dec16(smw);
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const uint32_t q2 = ((lo >> (2 * p)) & 0x00030003u) | (((hi >> p) & 0x00010001u) << 2);
-    const float qe = (float)(q2 & 0xFFu), qo = (float)(q2 >> 16);
-    out[p] = pack_f16(__builtin_fmaf(s, qe, m), __builtin_fmaf(s, qo, m));
+    const uint32_t h2 = ((hi >> p) & 0x00010001u) << 2;
+    out[p] = dec_pair(and_or(lo >> (2 * p), 0x00030003u, 0x64006400u | h2), d);
   }
 }
 
@@ -428,8 +448,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
       // buffer s & 1; A runs two K-steps ahead in sa0/sa1 (even/odd stages), B
       // pairs in bp0 (stages 4j, 4j+1) and bp1 (4j+2, 4j+3); loads past the end
       // repeat the last K-step or pair and are never used.
-      struct BPair {
-        uint4 c[BITS / 2];
+      struct BPair {  // a row's codes for two K-steps (BITS words each) and both scale/min words
+        uint32_t w[2 * BITS];
         uint2 sm;
       };
       // Buffer loads: a 32-bit per-lane offset from a workgroup-uniform base,
@@ -450,32 +470,43 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
           a[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, a_voff[jj], ks * kBK * 2, 0));
       };
       auto load_bpair = [&](BPair& bp, int ks) {  // ks even, ks + 1 < KS
+        if constexpr (BITS == 3) {  // 24 bytes, 8-byte aligned: three 8-byte loads
 #pragma unroll
-        for (int j = 0; j < BITS / 2; ++j)
-          bp.c[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bc_voff + 16 * j, ks * (4 * BITS), 0));
+          for (int j = 0; j < 3; ++j) {
+            const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bc_voff + 8 * j,
+                                                                                             ks * (4 * BITS), 0));
+            bp.w[2 * j] = v.x;
+            bp.w[2 * j + 1] = v.y;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < BITS / 2; ++j) {
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bc_voff + 16 * j,
+                                                                                              ks * (4 * BITS), 0));
+            bp.w[4 * j] = v.x;
+            bp.w[4 * j + 1] = v.y;
+            bp.w[4 * j + 2] = v.z;
+            bp.w[4 * j + 3] = v.w;
+          }
+        }
         bp.sm = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bs_voff, ks * 4, 0));
       };
       auto store_bpair = [&](const BPair& bp, int e, int buf) {  // e: which K-step of the pair
+        // K-step e's words: 2-bit (half 0, half 1); 3-bit (low bits of half 0,
+        // of half 1, high bits); 4-bit (two words per half)
+        const uint32_t* c = bp.w + e * BITS;
         uint32_t code[B_HALVES][BITS == 2 ? 1 : 2];
-        if constexpr (B_HALVES == 2) {
+#pragma unroll
+        for (int hh = 0; hh < B_HALVES; ++hh) {
+          const int h = B_HALVES == 2 ? hh : b_half0;  // two threads per row: each its half
           if constexpr (BITS == 2) {
-            code[0][0] = e ? bp.c[0].z : bp.c[0].x;
-            code[1][0] = e ? bp.c[0].w : bp.c[0].y;
+            code[hh][0] = h ? c[1] : c[0];
+          } else if constexpr (BITS == 3) {
+            code[hh][0] = h ? c[1] : c[0];
+            code[hh][1] = h ? c[2] >> 8 : c[2];
           } else {
-            const uint4 c = bp.c[e];
-            code[0][0] = c.x;
-            code[0][1] = c.y;
-            code[1][0] = c.z;
-            code[1][1] = c.w;
-          }
-        } else {  // two threads per row: each decodes its half, b_half0
-          if constexpr (BITS == 2) {
-            const uint32_t lo = e ? bp.c[0].z : bp.c[0].x, hi = e ? bp.c[0].w : bp.c[0].y;
-            code[0][0] = b_half0 ? hi : lo;
-          } else {
-            const uint4 c = bp.c[e];
-            code[0][0] = b_half0 ? c.z : c.x;
-            code[0][1] = b_half0 ? c.w : c.y;
+            code[hh][0] = h ? c[2] : c[0];
+            code[hh][1] = h ? c[3] : c[1];
           }
         }
         store_b(code, e ? bp.sm.y : bp.sm.x, buf);
@@ -723,7 +754,7 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   const int tiles_pad = (int)ceil_div(max_tiles, kXcd) * kXcd;  // whole rounds over the dies
   // The pair kernel addresses x, h and an expert blob with 32-bit byte offsets.
   constexpr int64_t kOff = int64_t(1) << 31;
-  constexpr bool kPairOk = BITS != 3;  // the pair loads assume 8- or 16-byte K-steps
+  constexpr bool kPairOk = true;
   const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
   if (kPairOk && off_ok && q.H % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk, kNT>,
