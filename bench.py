@@ -49,15 +49,15 @@ BF16_PEAK_TFLOPS = 2500.0
 
 # Memory traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two runs), scaled
 # by what the same counters read for a plain 256 MiB device-to-device copy in the same runs (FETCH_SIZE reads
-# 131,088 KiB for it: x1.99975; WRITE_SIZE reads 262,144 KiB: x1.0).  Each entry is valid only for the kernel
+# 131,093.5 KiB for it: x1.99968; WRITE_SIZE reads 262,144 KiB: x1.0).  Each entry is valid only for the kernel
 # sources it was measured on (first 16 hex digits of their SHA-256); after a change the traffic is reported null.
-FETCH_SCALE = 262144.0 / 131088.1875
+FETCH_SCALE = 262144.0 / 131093.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "d619ef0351924a89",
-                    "fetch_kib": 7632.3, "write_kib": 62.9},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "344d26f0b49b6274", "fetch_kib": 384532.0,
-                    "write_kib": 88696.5},
+    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "b40f4213d879d35c",
+                    "fetch_kib": 7630.0, "write_kib": 62.9},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "73aaa40622a3bb55", "fetch_kib": 396369.3,
+                    "write_kib": 87933.0},
 }
 
 
