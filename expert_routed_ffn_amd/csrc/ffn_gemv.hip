@@ -13,8 +13,9 @@
 //   sum_c (s*q_c + m) x_c = s * sum_c (128 + q_c) x_c + (m - 128*s) * sum_c x_c.
 // (128 + q) is a bf16 whose bit pattern is 0x4300 | q, so two codes become a
 // packed bf16 pair with one shift and one and-or (the code layout puts
-// adjacent columns in the two halfwords of a word), and v_dot2c_f32_bf16 does
-// the two MACs against the packed input pair with fp32 accumulation.
+// adjacent columns in the two halfwords of a word; 3-bit codes or in their high
+// bits from the block's third word), and v_dot2c_f32_bf16 does the two MACs
+// against the packed input pair with fp32 accumulation.
 // sum_c x_c is per input row and chunk, computed once per wave.  Inputs that
 // are not bf16 (fp32 activations, h) are carried as an unevaluated sum
 // hi + lo of two bf16 values (about 16 significant bits), so the products

@@ -23,7 +23,7 @@
  *  - Weights.  The engine's fast size is a 2-bit class quantization (Q2_0)
  *    (same page, speed table in section "3. 바로 써먹기"); the format used here
  *    is blocks of 32 weights along each row with an fp16 scale s and fp16 min
- *    m and b-bit unsigned codes (b = 2 or 4), weight = s*q + m.  Bytes per
+ *    m and b-bit unsigned codes (b = 2, 3 or 4), weight = s*q + m.  Bytes per
  *    weight = b/8 + 4/32, the same block-32 accounting that gives the 0.5625
  *    bytes/value printed for Q4_0 on the KATANA page (trawling.dev/post/3323,
  *    section "실행 환경과 메모리 구성").
@@ -31,8 +31,12 @@
  *
  * Byte layout (decoded here from its description, not from any other code):
  *   code plane of a [R x K] matrix: per row K*b/32 little-endian 32-bit words;
- *   word w holds columns w*(32/b) .. w*(32/b) + 32/b - 1; column c of the word
- *   is at bit 16*(c mod 2) + b*floor(c/2).
+ *   b = 2, 4: word w holds columns w*(32/b) .. w*(32/b) + 32/b - 1; column c of
+ *   the word is at bit 16*(c mod 2) + b*floor(c/2).  b = 3 (3-bit size classes
+ *   are ranked on the same page; their layout is not given there, so this one
+ *   is a reading): three words per 32-column block, the low two bits of each
+ *   code in words 0-1 laid out as for b = 2, the high bit of block column j in
+ *   word 2 at bit 16*(j mod 2) + floor(j/2).
  *   scale/min plane: per row K/32 words; low half = scale, high half = min
  *   (IEEE binary16 each).
  *   expert blob: Wg codes, Wg s/m, Wu codes, Wu s/m, Wd codes, Wd s/m, each

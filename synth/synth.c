@@ -15,11 +15,13 @@
  * Weight encoding (the format the layer decodes):
  *   a matrix [R x K] (rows K-contiguous, K % 32 == 0) is cut into blocks of 32
  *   weights along K.  Each block has an IEEE binary16 scale s and min m and
- *   b-bit unsigned codes q (b = 2 or 4); the weight it stands for is s*q + m.
- *   Code plane: each row is K*b/32 little-endian 32-bit words; word w holds
- *   columns [w*32/b, (w+1)*32/b); column c of the word (0 <= c < 32/b) sits at
- *   bit 16*(c % 2) + b*(c / 2).  Even columns fill the low halfword, odd
- *   columns the high halfword.
+ *   b-bit unsigned codes q (b = 2, 3 or 4); the weight it stands for is s*q + m.
+ *   Code plane: each row is K*b/32 little-endian 32-bit words.  b = 2, 4: word
+ *   w holds columns [w*32/b, (w+1)*32/b); column c of the word (0 <= c < 32/b)
+ *   sits at bit 16*(c % 2) + b*(c / 2).  Even columns fill the low halfword,
+ *   odd columns the high halfword.  b = 3: three words per 32-column block, the
+ *   low two bits of the codes in words 0-1 as for b = 2, the high bits in word
+ *   2 (block column j at bit 16*(j % 2) + j / 2).
  *   Scale/min plane: one 32-bit word per block, row-major [R][K/32]; low
  *   halfword = scale, high halfword = min.
  *   Expert blob: Wg codes, Wg s/m, Wu codes, Wu s/m, Wd codes, Wd s/m, each
