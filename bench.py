@@ -591,7 +591,7 @@ def stack125b_bench(args, torch, moe, synth, oracle):
     dbufs = {"ids": ids, "w": wt, "dispatch": d, "y": y, "out": out,
              "dws": torch.zeros(moe.decode_workspace_bytes(views[0], T, k), dtype=torch.uint8, device=dev)}
 
-    def dstep(s):  # moe_layer_decode_slots: routing + resolve in one workgroup, miss copy, gate/up, down + combine
+    def dstep(s):  # moe_layer_decode_slots: routing + resolve in one workgroup, gate/up staging the misses, down
         for l in range(L):
             moe.layer_decode_slots(table, l, views[l], x_d[s, l], lg_d[s, l], k, residual=x_d[s, l],
                                    out_bf16=rec[s, l], bufs=dbufs)
@@ -625,9 +625,10 @@ def stack125b_bench(args, torch, moe, synth, oracle):
                 "hit_rate": hits / max(1, hits + misses), "misses_per_step": misses / steps,
                 "h2d_MB_per_step": h2d / steps / 1e6, "h2d_GBs_effective_share": h2d / steps / sec_d / 1e9,
                 "bit_identical_to_resident": True,
-                "note": "moe_layer_decode_slots: the policy runs in the routing workgroup and the misses are "
-                        "copied by a kernel reading the page-locked master copy through its device mapping; no host "
-                        "round trip, steps captured in graphs"}
+                "note": "moe_layer_decode_slots: the policy runs in the routing workgroup; the gate/up launch "
+                        "reads the missed experts' gate/up rows from the page-locked master copy (device mapping) "
+                        "and writes them into their slots while the resident experts' rows run, and its copy "
+                        "workgroups move the rest of each missed blob; no host round trip, steps captured in graphs"}
     print(f"[stack125b] slots, device policy: {sec_d * 1e6:.1f} us/step", file=sys.stderr, flush=True)
     return {
         "metric": "MoE stack tokens/s (125B-shaped stack, decode T=3)",

@@ -30,6 +30,11 @@ ProfileReq& profile_req() {
 
 static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 
+#ifndef MOE_STAGE_IN_GATEUP
+#define MOE_STAGE_IN_GATEUP 1
+#endif
+constexpr bool kStageInGateup = MOE_STAGE_IN_GATEUP != 0;
+
 BlobLayout blob_layout(int H, int I, int bits) {
   const int64_t gu_codes = (int64_t)I * H * bits / 8, gu_sm = (int64_t)I * (H / 32) * 4;
   const int64_t d_codes = (int64_t)H * I * bits / 8, d_sm = (int64_t)H * (I / 32) * 4;
@@ -292,7 +297,12 @@ moe_status moe_layer_decode_slots(const moe_qlayer* q, moe_slot_table* t, int la
   if (moe_status st = launch_route_dispatch_resolve(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
                                                     active, n_active, W, t, layer, stream))
     return st;
-  if (moe_status st = launch_slot_copy(t, stream)) return st;
+  // Wide shapes stage the misses inside the gate/up launch, overlapping their
+  // transfer with the resident experts' rows; other shapes copy them first.
+  const bool stage = kStageInGateup && gemv_stages_misses(q->H, q->I);
+  if (!stage)
+    if (moe_status st = launch_slot_copy(t, stream)) return st;
+  const MissStage ms{v.copies, v.ncopies, v.host_dev};
   FoldedCombine fc;
   const bool fold = gemv_folds_combine(q->H, q->I);
   if (fold) {
@@ -302,7 +312,8 @@ moe_status moe_layer_decode_slots(const moe_qlayer* q, moe_slot_table* t, int la
     fc.out = out;
     fc.out_bf16 = out_bf16;
   }
-  if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, fc, stream))
+  if (moe_status st = launch_ffn_gemv_steps(*q, x, x_t, T, k, sorted_assign, n_active, W, y, y_t, fc, stream,
+                                            stage ? &ms : nullptr))
     return st;
   return fold ? MOE_OK : launch_combine(y, y_t, w, T, k, q->H, residual, r_t, out, out_bf16, stream);
 }

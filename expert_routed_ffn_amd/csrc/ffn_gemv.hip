@@ -182,6 +182,21 @@ __device__ __forceinline__ void load_codes(uint32_t (&code)[BITS], const uint8_t
   }
 }
 
+// Writes back what load_codes read, as a buffer store at lane offset `lo`
+// plus the wave-uniform offset `so` of a resource over the destination blob
+// (no 64-bit address registers held for it).
+template <int BITS>
+__device__ __forceinline__ void store_codes_buf(__amdgpu_buffer_rsrc_t rd, uint32_t lo, uint32_t so,
+                                                const uint32_t (&code)[BITS]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  so = __builtin_amdgcn_readfirstlane(so);
+  if constexpr (BITS == 2) __builtin_amdgcn_raw_buffer_store_b64(u32x2{code[0], code[1]}, rd, lo, so, 0);
+  else if constexpr (BITS == 3) __builtin_amdgcn_raw_buffer_store_b96(u32x3{code[0], code[1], code[2]}, rd, lo, so, 0);
+  else __builtin_amdgcn_raw_buffer_store_b128(u32x4{code[0], code[1], code[2], code[3]}, rd, lo, so, 0);
+}
+
 __device__ __forceinline__ float group_sum(float v, int G) {
   for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
@@ -594,9 +609,12 @@ __device__ __forceinline__ void make_chunk(XChunk<SPLIT>& c, const RawX<SPLIT>& 
 constexpr int kWideTM = 3;  // routed rows per pass in the wide gate/up kernel
 template <bool SPLIT> constexpr int kWideNI = SPLIT ? MOE_WIDE_NI_SPLIT : MOE_WIDE_NI;
 
-template <int BITS, int NT, bool SPLIT, int NI>
+// STAGE: blob is a missed expert's master copy, and when dst is set the
+// pass also writes every code and s/m word it reads (rows below I) to the
+// same offsets of dst, the expert's slot.
+template <int BITS, int NT, bool SPLIT, int NI, bool STAGE = false>
 __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int i0,
-                                                 int rel0) {
+                                                 int rel0, uint8_t* dst = nullptr) {
   const int lane = threadIdx.x & 63;
   const int64_t rcb = (int64_t)A.H * BITS / 8, rsb = (int64_t)(A.H / 32) * 4;
   int64_t tok[NT];
@@ -625,6 +643,24 @@ __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot
       sg[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_gs + ri[r] * rsb + chunk * 4);
       load_codes<BITS>(cu[r], blob + A.off_uc + ri[r] * rcb + chunk * (4 * BITS));
       su[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_us + ri[r] * rsb + chunk * 4);
+    }
+    if constexpr (STAGE) {
+      // Buffer stores through a resource over dst; without dst the resource
+      // has no records and the hardware drops every store (no branch, no
+      // traffic).  Offsets fit in 32 bits: an expert blob is far below 4 GiB.
+      // Rows past I repeat row I - 1 and rewrite its bytes unchanged.
+      const __amdgpu_buffer_rsrc_t rd =
+          __builtin_amdgcn_make_buffer_rsrc(dst ? dst : const_cast<uint8_t*>(blob), (short)0, dst ? -1 : 0, 0x00020000);
+      const uint32_t lc = (uint32_t)(chunk * (4 * BITS)), ls = (uint32_t)(chunk * 4);
+#pragma unroll
+      for (int r = 0; r < NI; ++r) {
+        store_codes_buf<BITS>(rd, lc, (uint32_t)(A.off_gc + ri[r] * rcb), cg[r]);
+        __builtin_amdgcn_raw_buffer_store_b32(sg[r], rd, ls,
+                                              __builtin_amdgcn_readfirstlane((uint32_t)(A.off_gs + ri[r] * rsb)), 0);
+        store_codes_buf<BITS>(rd, lc, (uint32_t)(A.off_uc + ri[r] * rcb), cu[r]);
+        __builtin_amdgcn_raw_buffer_store_b32(su[r], rd, ls,
+                                              __builtin_amdgcn_readfirstlane((uint32_t)(A.off_us + ri[r] * rsb)), 0);
+      }
     }
     XChunk<SPLIT> xc[NT];
 #pragma unroll
@@ -665,8 +701,33 @@ __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot
   }
 }
 
-template <int BITS, int TM, bool SPLIT, int NI>
-__device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot& d, int j) {
+// Misses of a device-mode resolve staged by the gate/up launch (MissStage on
+// the host side).  The first ncw workgroups of the grid copy the bytes of each
+// missed blob that no gate/up item writes: everything outside the gate and up
+// code and s/m planes, i.e. the down planes and the padding between planes.
+struct StageArgs {
+  const int32_t* copies;   // [2 * n] (slot, l*E + e)
+  const int32_t* ncopies;  // [1] n
+  const uint8_t* host;     // device view of the master copy, blob l*E + e at (l*E + e) * stride
+  int64_t item_lo[4], item_hi[4];  // byte ranges [lo, hi) of the blob the gate/up items write
+  int ncw;                 // copy workgroups at the front of the grid
+};
+
+// The master blob of slot `idx` if this step's resolve listed it as a miss,
+// else null.  Wave-uniform.
+__device__ __forceinline__ const uint8_t* staged_source(const StageArgs& G, int64_t stride, int idx) {
+  const int lane = threadIdx.x & 63, nc = *G.ncopies;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const int c = c0 + lane;
+    const uint64_t m = __ballot(c < nc && G.copies[2 * c] == idx);
+    if (m) return G.host + (int64_t)G.copies[2 * (c0 + __builtin_ctzll(m)) + 1] * stride;
+  }
+  return nullptr;
+}
+
+template <int BITS, int TM, bool SPLIT, int NI, bool STAGE = false>
+__device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot& d, int j,
+                                                 const StageArgs* G = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i0 = (j * 4 + wave) * NI;
   if (i0 >= A.I) return;
@@ -681,12 +742,56 @@ __device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot
     return;
   }
   const uint8_t* blob = A.base + (int64_t)idx * A.stride;
+  uint8_t* dst = nullptr;
+  if constexpr (STAGE) {
+    // a miss: every pass reads the master copy, the first one also fills the slot
+    if (const uint8_t* src = staged_source(*G, A.stride, idx)) {
+      dst = const_cast<uint8_t*>(blob);
+      blob = src;
+    }
+  }
   for (int tg = 0; tg < d.ne;) {
     const int nt = min(d.ne - tg, TM);
-    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT, NI>(A, d, blob, i0, tg);
-    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT, NI>(A, d, blob, i0, tg);
-    else gateup_pass_wide<BITS, 1, SPLIT, NI>(A, d, blob, i0, tg);
+    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
+    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
+    else gateup_pass_wide<BITS, 1, SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
     tg += nt;
+    dst = nullptr;
+  }
+}
+
+constexpr int kStageUnroll = 4;
+constexpr int64_t kStageChunk = (int64_t)256 * 16 * kStageUnroll;  // bytes per copy work item
+
+// Copy workgroup `cw` of G.ncw: work items of kStageChunk bytes over the
+// missed blobs, 16 bytes per thread per step, skipping what the items write
+// (those ranges start on 256-byte boundaries and their lengths are multiples
+// of 128 bytes, so no 16-byte piece straddles one).
+__device__ __forceinline__ void stage_copy(const StageArgs& G, uint8_t* slots, int64_t eb, int cw) {
+  const int nc = *G.ncopies;
+  const int64_t cpb = (eb + kStageChunk - 1) / kStageChunk;
+  const int64_t total = (int64_t)nc * cpb;
+  for (int64_t w = cw; w < total; w += G.ncw) {
+    const int c = (int)(w / cpb);
+    const int64_t ch = w % cpb;
+    const uint8_t* src = G.host + (int64_t)G.copies[2 * c + 1] * eb;
+    uint8_t* dst = slots + (int64_t)G.copies[2 * c] * eb;
+    uint4 v[kStageUnroll];
+    bool on[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int64_t off = ch * kStageChunk + ((int64_t)u * 256 + threadIdx.x) * 16;
+      bool mine = off < eb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) mine = mine && !(off >= G.item_lo[p] && off < G.item_hi[p]);
+      on[u] = mine;
+      if (mine) v[u] = *reinterpret_cast<const uint4*>(src + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int64_t off = ch * kStageChunk + ((int64_t)u * 256 + threadIdx.x) * 16;
+      if (on[u]) *reinterpret_cast<uint4*>(dst + off) = v[u];
+    }
   }
 }
 
@@ -851,6 +956,23 @@ __global__ __launch_bounds__(256) void ffn_gateup_kernel(DecodeArgs A) {
   else item_gateup<BITS, TM, SPLIT, SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>>(A, d, j);
 }
 
+// Gate/up of moe_layer_decode_slots with the misses staged in the same
+// launch: workgroups [0, ncw) copy, the rest are the wide gate/up items.
+template <int BITS, int TM, bool SPLIT>
+__global__ __launch_bounds__(256) void ffn_gateup_stage_kernel(DecodeArgs A, StageArgs G) {
+  if ((int)blockIdx.x < G.ncw) {
+    stage_copy(G, const_cast<uint8_t*>(A.base), A.stride, (int)blockIdx.x);
+    return;
+  }
+  const int b = (int)blockIdx.x - G.ncw;
+  const int s = b / A.TA, j = b % A.TA;
+  Slot d = load_slot(A, s);
+  if (d.e < 0) return;  // slot past the active experts
+  const int lane = threadIdx.x & 63;
+  d.tokv = lane < kDescT ? d.p->tok[lane] : 0;
+  item_gateup_wide<BITS, TM, SPLIT, kWideNI<SPLIT>, true>(A, d, j, &G);
+}
+
 // Down (general shapes): one workgroup per (active expert, tile of H).
 template <int BITS, int TM, bool YBF16>
 __global__ __launch_bounds__(256) void ffn_down_kernel(DecodeArgs A) {
@@ -905,6 +1027,27 @@ moe_status launch_wide(DecodeArgs& a, int max_active, hipStream_t s) {
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
            dim3(64 * kRowWaves), 0, s, a);
   return check_launch("ffn_down");
+}
+
+// Copy workgroups of the staging gate/up launch.
+constexpr int kStageCopyGroups = 64;
+
+template <int BITS, bool SPLIT, bool YBF16>
+moe_status launch_wide_stage(DecodeArgs& a, const StageArgs& g, int max_active, hipStream_t s) {
+  a.TA = (int)ceil_div(a.I, 4 * kWideNI<SPLIT>);
+  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_gateup_stage_kernel<BITS, kWideTM, SPLIT>,
+           dim3((unsigned)(g.ncw + max_active * a.TA)), dim3(256), 0, s, a, g);
+  if (moe_status st = check_launch("ffn_gateup_stage")) return st;
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
+           dim3(64 * kRowWaves), 0, s, a);
+  return check_launch("ffn_down");
+}
+
+template <bool SPLIT, bool YBF16>
+moe_status launch_stage_b(DecodeArgs& a, const StageArgs& g, int bits, int max_active, hipStream_t s) {
+  return bits == 2   ? launch_wide_stage<2, SPLIT, YBF16>(a, g, max_active, s)
+         : bits == 3 ? launch_wide_stage<3, SPLIT, YBF16>(a, g, max_active, s)
+                     : launch_wide_stage<4, SPLIT, YBF16>(a, g, max_active, s);
 }
 
 // ---- decode step with the routing inside the gate/up launch ----------------------
@@ -1062,9 +1205,11 @@ size_t ffn_gemv_ws_bytes(int T, int k, int E, int H, int I) { return decode_ws(n
 
 bool gemv_folds_combine(int H, int I) { return wide_shape(H, I); }
 
+bool gemv_stages_misses(int H, int I) { return wide_shape(H, I); }
+
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
-                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s) {
+                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s, const MissStage* ms) {
   DecodeArgs a = make_args(q, x, T, k, sorted_assign, n_active, W, y);
   if (fc.out) {
     if (!wide_shape(q.H, q.I) || (int64_t)T * k > kDecodeMaxRows || T * kRowTile > 64 * kRowWaves)
@@ -1077,6 +1222,28 @@ moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x
   }
   const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
   const bool split = x_t == MOE_F32, yb = y_t == MOE_BF16;
+  if (ms) {
+    if (!wide_shape(q.H, q.I)) return fail(MOE_EUNSUPPORTED, "misses cannot be staged in the gate/up launch");
+    const BlobLayout L = blob_layout(q.H, q.I, q.bits);
+    const int64_t codes = (int64_t)q.I * q.H * q.bits / 8, sm = (int64_t)q.I * (q.H / 32) * 4;
+    StageArgs g{};
+    g.copies = ms->copies;
+    g.ncopies = ms->ncopies;
+    g.host = ms->host;
+    g.item_lo[0] = L.gate_codes;
+    g.item_hi[0] = L.gate_codes + codes;
+    g.item_lo[1] = L.gate_sm;
+    g.item_hi[1] = L.gate_sm + sm;
+    g.item_lo[2] = L.up_codes;
+    g.item_hi[2] = L.up_codes + codes;
+    g.item_lo[3] = L.up_sm;
+    g.item_hi[3] = L.up_sm + sm;
+    g.ncw = kStageCopyGroups;
+    if (split) return yb ? launch_stage_b<true, true>(a, g, q.bits, max_active, s)
+                         : launch_stage_b<true, false>(a, g, q.bits, max_active, s);
+    return yb ? launch_stage_b<false, true>(a, g, q.bits, max_active, s)
+              : launch_stage_b<false, false>(a, g, q.bits, max_active, s);
+  }
   if (split)
     return yb ? launch_b<true, true>(a, q.bits, T, max_active, s) : launch_b<true, false>(a, q.bits, T, max_active, s);
   return yb ? launch_b<false, true>(a, q.bits, T, max_active, s) : launch_b<false, false>(a, q.bits, T, max_active, s);

@@ -100,6 +100,9 @@ struct SlotTableView {
   size_t expert_bytes;
   const uint8_t* slots;
   const int32_t* map;
+  const uint8_t* host_dev;  // device view of the master copy (device mode)
+  const int32_t* copies;    // the last device resolve's misses, [2 * n] (slot, l*E + e)
+  const int32_t* ncopies;   // [1] n
 };
 bool slot_table_device_mode(const moe_slot_table* t);
 SlotDevArgs slot_dev_args(const moe_slot_table* t);
@@ -111,9 +114,22 @@ moe_status launch_route_dispatch_resolve(const float* logits, int T, int E, int 
                                          int32_t* active, int32_t* n_active, const DecodeWs& W,
                                          const moe_slot_table* t, int layer, hipStream_t s);
 
+// The misses of a device-mode resolve, staged inside the gate/up launch
+// instead of by a copy kernel before it (wide shapes only, see
+// gemv_stages_misses): the gate/up rows of a missed expert are read from the
+// master copy and written into its slot as they are used, and workgroups at
+// the front of the same grid copy the rest of each missed blob.
+struct MissStage {
+  const int32_t* copies = nullptr;   // [2 * n] (slot, l*E + e) of the resolve's misses
+  const int32_t* ncopies = nullptr;  // [1] n
+  const uint8_t* host = nullptr;     // device view of the page-locked master copy
+};
+bool gemv_stages_misses(int H, int I);
+
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,
-                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s);
+                                 moe_dtype y_t, const FoldedCombine& fc, hipStream_t s,
+                                 const MissStage* ms = nullptr);
 
 size_t ffn_mfma_ws_bytes(int T, int k, int E, int H, int I);
 moe_status launch_ffn_mfma(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,

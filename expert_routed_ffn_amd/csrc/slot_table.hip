@@ -483,7 +483,8 @@ SlotDevArgs slot_dev_args(const moe_slot_table* t) {
 }
 
 SlotTableView slot_table_view(const moe_slot_table* t) {
-  return SlotTableView{t->L, t->E, t->n_slots, t->expert_bytes, t->slots, t->slot_map_dev};
+  return SlotTableView{t->L,      t->E,        t->n_slots,  t->expert_bytes, t->slots,
+                       t->slot_map_dev, t->host_dev, t->d_copies, t->d_ncopies};
 }
 
 moe_status launch_slot_copy(const moe_slot_table* t, hipStream_t stream) {

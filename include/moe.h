@@ -298,9 +298,16 @@ size_t moe_slot_table_device_bytes(int L, int E, int n_slots);
 /*
  * moe_layer_decode_slots -- moe_layer_decode through a slot table in device
  * mode: the routing workgroup also resolves the routed experts of `layer`
- * (moe_slot_table_resolve_device's policy), then the misses are copied in and
- * the gate/up and down kernels run on the slots (four launches, or five when
- * the combine cannot be folded).  q must be the table's view of `layer`:
+ * (moe_slot_table_resolve_device's policy), then the gate/up and down kernels
+ * run on the slots.  Strata feature (tech.hub77a.com), section
+ * "2. 왜 대단한가" (2): resident experts are used at once while the missing
+ * ones move in from host RAM.  When H % 2048 == 0 and I % 512 == 0 the misses
+ * are staged inside the gate/up launch (three launches): the gate/up rows of
+ * a missed expert are read from the master copy and written into its slot as
+ * they are used, while the resident experts' rows run beside them and
+ * workgroups of the same grid copy the rest of each missed blob.  Other
+ * shapes copy the misses in a launch of their own first (four launches, or
+ * five when the combine cannot be folded).  q must be the table's view of `layer`:
  * base = slots, stride = expert_bytes, slot_map = map + layer * E.  Outputs
  * and workspace as moe_layer_decode (moe_layer_decode_workspace_bytes); every
  * output is bit-identical to moe_layer_decode on resident weights.

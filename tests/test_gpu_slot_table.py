@@ -235,12 +235,15 @@ def test_slot_table_device_mode_errors(moe):
     table.close()
 
 
-@pytest.mark.parametrize("n_slots", [64, 30])
-def test_layer_decode_slots_matches_resident_layer_decode(moe, n_slots):
-    """moe_layer_decode_slots (router + resolve in one workgroup, copy, FFN) against moe_layer_decode on resident
-    weights, and the table's counters against the stand-alone device resolve on the same steps."""
+@pytest.mark.parametrize("bits,T,n_slots,xf32", [(2, 3, 64, False), (2, 3, 30, False), (3, 5, 64, False),
+                                                  (4, 12, 64, False), (2, 7, 64, True)])
+def test_layer_decode_slots_matches_resident_layer_decode(moe, bits, T, n_slots, xf32):
+    """moe_layer_decode_slots (router + resolve in one workgroup, then the gate/up launch that also stages the
+    misses, then down) against moe_layer_decode on resident weights, and the table's counters against the
+    stand-alone device resolve on the same steps.  T above 3 takes several gate/up passes per item, of which
+    only the first fills the slot."""
     import torch
-    w = _stack(H=2048, I=512, E=64, k=10)  # wide shape: the combine is folded into the down kernel
+    w = _stack(H=2048, I=512, E=64, k=10, bits=bits, T=T)  # wide shape: the combine is folded into the down kernel
     eb = w.expert_bytes
     host = _host_master(w, torch)
     dev_all = host.to("cuda")
@@ -257,6 +260,8 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, n_slots):
     for s in range(3):
         x = torch.from_numpy(w.x(0, s).view(np.int16).copy()).view(torch.bfloat16).cuda()
         for l in range(w.layers):
+            if xf32:
+                x = x.float()
             lg = torch.from_numpy(synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, l, s), w.T, w.E,
                                                synth.drifted_bias(w, l, s, 0.05))).cuda()
             a = moe.layer_decode(resident[l], x, lg, w.k, residual=x)
@@ -271,7 +276,8 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, n_slots):
     assert np.array_equal(fused.map_host(), split.map_host())
     assert fused.stats()["misses"] > 0
     # every filled slot holds its expert's master blob: the gate and up planes
-    # written by the read-through items, the rest by the side-stream copy
+    # written by the gate/up items that read the master copy, the rest by the
+    # copy workgroups of the same launch
     smap = fused.map_host().reshape(-1)
     slots_h = fused.slots.cpu().numpy()
     host_h = host.numpy()
