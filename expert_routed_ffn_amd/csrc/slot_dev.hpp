@@ -10,7 +10,8 @@
 // stamps the hits in active order, then gives each miss, in ascending expert
 // id, the slot with the smallest stamp: every slot of this resolve has a
 // larger stamp than all others, so none is a victim while n_active <= n_slots.
-// The (slot, blob) pairs of the misses are listed for a copy kernel.
+// The (slot, blob) pairs of the misses are listed for the copy (a copy kernel,
+// or the gate/up launch that stages them).
 #pragma once
 
 #include <cstdint>
