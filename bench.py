@@ -291,7 +291,27 @@ def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2):
     for _ in range(args.prefill_steps):
         step()
     torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / args.prefill_steps
+    eager_out = bufs["out"].clone()
+
+    # the same steps captured in one graph, as a serving loop replays a chunk's launches: no host gaps between
+    # the nine kernels of a step; two replays, each checked against the eager result
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        for _ in range(args.prefill_steps):
+            step()
+    g.replay()  # untimed (graph upload)
+    torch.cuda.synchronize()
+    if not torch.equal(bufs["out"], eager_out):
+        raise SystemExit("bench: prefill graph replay differs from the eager step")
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
     el = (time.perf_counter() - t0) / args.prefill_steps
+    if not torch.equal(bufs["out"], eager_out):
+        raise SystemExit("bench: prefill graph replay differs from the eager step")
+    del g
 
     n = T * k
     timer = KernelTimer(2 * args.prefill_steps)
@@ -314,6 +334,8 @@ def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2):
         "value": T / el,
         "unit": "tokens/s",
         "ms_per_step": el * 1e3,
+        "hip_graph": True,
+        "eager_ms_per_step": eager * 1e3,
         "layer_tflops": (gu_flops + dn_flops) / el / 1e12,
         "experts_hit": int((counts > 0).sum()),
         "max_rows_per_expert": int(counts.max()),
