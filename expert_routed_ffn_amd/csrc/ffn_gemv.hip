@@ -609,9 +609,9 @@ __device__ __forceinline__ void make_chunk(XChunk<SPLIT>& c, const RawX<SPLIT>& 
 constexpr int kWideTM = 3;  // routed rows per pass in the wide gate/up kernel
 template <bool SPLIT> constexpr int kWideNI = SPLIT ? MOE_WIDE_NI_SPLIT : MOE_WIDE_NI;
 
-// STAGE: blob is a missed expert's master copy, and when dst is set the
-// pass also writes every code and s/m word it reads (rows below I) to the
-// same offsets of dst, the expert's slot.
+// STAGE: when dst is set, blob is a missed expert's master copy and the pass
+// also writes every code and s/m word it reads to the same offsets of dst,
+// the expert's slot.
 template <int BITS, int NT, bool SPLIT, int NI, bool STAGE = false>
 __device__ __forceinline__ void gateup_pass_wide(const DecodeArgs& A, const Slot& d, const uint8_t* blob, int i0,
                                                  int rel0, uint8_t* dst = nullptr) {
