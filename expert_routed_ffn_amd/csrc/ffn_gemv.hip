@@ -807,8 +807,14 @@ constexpr int kRowTile = 8;
 constexpr int kRowWaves = 16;
 constexpr int kDecodeMaxRows = kDescT * kMaxK;  // routed rows a folded combine can hold (192)
 
+// pp: sorted positions below T*k, loaded unconditionally (so that no load
+// waits for the routed-row count); ok: whether the position is a routed row,
+// the only rows whose results are stored.  The expert id read for a position
+// past the routed rows is stale workspace, clamped into [0, E) so every load
+// stays inside the layer.
 template <int BITS, int NIT, bool YBF16>
-__device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (&pp)[NIT], int n0, float* ylds) {
+__device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (&pp)[NIT], const bool (&ok)[NIT],
+                                                int n0, float* ylds) {
   const int lane = threadIdx.x & 63, sl = lane >> 4, gl = lane & 15;
   const int64_t rcb = (int64_t)A.I * BITS / 8, rsb = (int64_t)(A.I / 32) * 4;
   int aa[NIT];
@@ -817,8 +823,8 @@ __device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (
   const uint8_t* blob[NIT];
 #pragma unroll
   for (int q = 0; q < NIT; ++q) {
-    pr[q] = pp[q] >= 0 ? pp[q] : 0;
-    const int e = A.rows[2 * pr[q]];
+    pr[q] = pp[q];
+    const int e = min(max(A.rows[2 * pr[q]], 0), A.E - 1);
     aa[q] = A.rows[2 * pr[q] + 1];
     const int idx = resident_index(A, e);
     res[q] = idx >= 0;
@@ -879,7 +885,7 @@ __device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (
   for (int q = 0; q < NIT; ++q) {
     float v[2] = {part[q][0], part[q][1]};
     reduce_scatter<2, 1, 3, 0>(v, lane);  // lanes with bit 3 clear hold row step 0, set: row step 1
-    if ((gl & 7) == 0 && pp[q] >= 0) {
+    if ((gl & 7) == 0 && ok[q]) {
       const int r = gl >> 3, n = n0 + 4 * r + sl;
       if (n < A.H) {
         const float val = res[q] ? v[0] : __builtin_nanf("");
@@ -915,16 +921,20 @@ __global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
                                        << 16)
                      : reinterpret_cast<const float*>(A.residual)[(size_t)ct * A.H + n0 + cr];
   }
-  const int nr = *A.nrows;
+  // Routed rows: nr <= T*k (fewer only when dispatch dropped ids).  The loop
+  // runs over T*k positions so that the row loads do not wait for nr.
+  const int nr = *A.nrows, nmax = A.T * A.k;
   float* yl = fold ? ylds : nullptr;
-  for (int p = wave; p < nr; p += 2 * kRowWaves) {
+  for (int p = wave; p < nmax; p += 2 * kRowWaves) {
     const int p2 = p + kRowWaves;
-    if (p2 < nr) {
+    if (p2 < nmax) {
       const int pp[2] = {p, p2};
-      down_rows_items<BITS, 2, YBF16>(A, pp, n0, yl);
+      const bool ok[2] = {p < nr, p2 < nr};
+      down_rows_items<BITS, 2, YBF16>(A, pp, ok, n0, yl);
     } else {
       const int pp[1] = {p};
-      down_rows_items<BITS, 1, YBF16>(A, pp, n0, yl);
+      const bool ok[1] = {p < nr};
+      down_rows_items<BITS, 1, YBF16>(A, pp, ok, n0, yl);
     }
   }
   if (!fold) return;
