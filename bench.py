@@ -54,7 +54,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FETCH_SCALE = 262144.0 / 131093.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "2aaf733452d07219",
+    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "8f6a01f8fbc49b43",
                     "fetch_kib": 7632.2, "write_kib": 62.9},
     "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "73aaa40622a3bb55", "fetch_kib": 396369.3,
                     "write_kib": 87933.0},
