@@ -158,10 +158,10 @@ moe_status moe_dispatch(const int32_t* ids, int T, int k, int E, int32_t* offset
   return launch_dispatch(ids, T * k, E, offsets, sorted_assign, assign_pos, active, n_active, ws, stream);
 }
 
-// AUTO: GEMV up to 256 routed rows, MFMA above.  On the 512-expert, top-10,
-// 2048 x 512 layer the two paths cross between T = 24 (GEMV 100 us, MFMA
-// 110 us per layer step) and T = 32 (118 us, 110 us).
-constexpr int64_t kAutoGemvMaxRows = 256;
+// AUTO: GEMV up to 128 routed rows, MFMA above.  On the 512-expert, top-10,
+// 2048 x 512 layer the two paths cross between T = 12 (GEMV 61 us, MFMA
+// 64 us per layer step) and T = 16 (77 us, 67 us).
+constexpr int64_t kAutoGemvMaxRows = 128;
 static moe_ffn_path resolve_path(moe_ffn_path p, int T, int k) {
   if (p == MOE_PATH_AUTO) return (int64_t)T * k <= kAutoGemvMaxRows ? MOE_PATH_GEMV : MOE_PATH_MFMA;
   return p;

@@ -78,7 +78,7 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Which expert-FFN kernels to run.  AUTO picks GEMV for T * k <= 256 routed rows
+/* Which expert-FFN kernels to run.  AUTO picks GEMV for T * k <= 128 routed rows
  * and MFMA above (the measured crossover on the 512-expert, top-10 decode layer). */
 typedef enum moe_ffn_path {
   MOE_PATH_AUTO = 0,

@@ -114,12 +114,12 @@ def test_layer_decode_argument_checks():
 
 
 def test_auto_path_workspace_follows_routed_rows():
-    """AUTO sizes its workspace for GEMV up to 256 routed rows (T * k) and for MFMA above."""
+    """AUTO sizes its workspace for GEMV up to 128 routed rows (T * k) and for MFMA above."""
     q = _q(E=512, H=2048, I=512)
     ws = lambda T, k, p: int(L.moe_expert_ffn_workspace_bytes(ctypes.byref(q), T, k, p))
     AUTO, GEMV, MFMA = 0, 1, 2
-    for T, k in [(1, 10), (25, 10), (32, 8), (26, 10), (64, 8), (8192, 10)]:
-        want = GEMV if T * k <= 256 else MFMA
+    for T, k in [(1, 10), (12, 10), (16, 8), (13, 10), (16, 10), (32, 8), (8192, 10)]:
+        want = GEMV if T * k <= 128 else MFMA
         assert ws(T, k, AUTO) == ws(T, k, want), (T, k)
     assert ws(26, 10, GEMV) != ws(26, 10, MFMA)
 
