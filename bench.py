@@ -751,6 +751,7 @@ def crossover_bench(args, torch, moe, synth, oracle):
         "workload": "512 experts, top-10, hidden 2048, intermediate 512, 2-bit, Zipf(1.1), bf16 x; 16 rotated "
                     "layer copies, graph-replayed steps",
         "unit": "us per layer step", "per_T": rows,
+        "first_T_mfma_faster": next((r["T"] for r in rows if r["mfma_us"] < r["gemv_us"]), None),
         "data": "synthetic",
     }
 
