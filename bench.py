@@ -56,8 +56,8 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "8f6a01f8fbc49b43",
                     "fetch_kib": 7632.2, "write_kib": 62.9},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "73aaa40622a3bb55", "fetch_kib": 396369.3,
-                    "write_kib": 87933.0},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "d4fdb911b67e081d", "fetch_kib": 297229.0,
+                    "write_kib": 83621.0},
 }
 
 

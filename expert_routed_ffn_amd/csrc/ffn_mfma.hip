@@ -59,6 +59,9 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 32;
 constexpr int kXcd = 8;  // accelerator dies (each with its own L2) that workgroups are spread over
+#ifndef MOE_MFMA_XCD_RANGE
+#define MOE_MFMA_XCD_RANGE 1  // 0: interleaved, 1: die ranges for gate/up, 2: for both GEMMs
+#endif
 // LDS tile rows: 0 = 80-byte pitch (padded); 1, 2 = 64-byte pitch with the
 // four 16-byte chunks of a row permuted by chunk ^ ((row >> SHIFT) & 3),
 // SHIFT = 2 or 1.  Measured on gfx950 with 128-bit reads in the fragment
@@ -271,8 +274,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
   // given consecutive blocks on the same die, which then reads the M-tile's
   // activation rows into its own L2 once for all of them.
   const int xcd = blockIdx.x % kXcd, j = blockIdx.x / kXcd;
-  const int tile_idx = (j / A.n_tiles_n) * kXcd + xcd, nt = j % A.n_tiles_n;
-  if (tile_idx >= *A.tile_count) return;
+  int tile_idx, nt;
+  if (MOE_MFMA_XCD_RANGE == 2 || (MOE_MFMA_XCD_RANGE == 1 && GATEUP)) {
+    // Each die takes one contiguous range of the M-tile list (expert order),
+    // so all M-tiles of an expert but those at a range boundary share one L2
+    // for the expert's weights, as the N-tiles of an M-tile share it for the
+    // activation rows.
+    const int count = *A.tile_count, per_die = (count + kXcd - 1) / kXcd, jt = j / A.n_tiles_n;
+    tile_idx = xcd * per_die + jt;
+    nt = j % A.n_tiles_n;
+    if (jt >= per_die || tile_idx >= count) return;
+  } else {
+    tile_idx = (j / A.n_tiles_n) * kXcd + xcd;
+    nt = j % A.n_tiles_n;
+    if (tile_idx >= *A.tile_count) return;
+  }
   const TileInfo ti = A.tiles[tile_idx];
   const int e = A.active[ti.slot];
   const int p_begin = A.offsets[e] + ti.m0;
