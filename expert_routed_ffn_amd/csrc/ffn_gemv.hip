@@ -1091,7 +1091,7 @@ constexpr int kRoutedNI = BITS >= 3 ? (SPLIT ? 2 : MOE_ROUTED_NI4) : (SPLIT ? MO
 // Workgroup 0 writes the routing and dispatch outputs (the down kernel and the
 // caller read them after the launch); every other workgroup routes in LDS,
 // reads its slot per wave and runs its gate/up rows.
-template <int BITS, bool SPLIT, int EPL>
+template <int BITS, bool SPLIT, int EPL, int NI>
 __global__ __launch_bounds__(256) void ffn_route_gateup_kernel(DecodeArgs A, RouteOut R) {
   __shared__ dev::RouterLds L;
   if (blockIdx.x == 0) {
@@ -1104,13 +1104,13 @@ __global__ __launch_bounds__(256) void ffn_route_gateup_kernel(DecodeArgs A, Rou
   const int b = blockIdx.x - 1, s = b / A.TA, j = b % A.TA;
   const dev::WaveSlot ws = dev::wave_slot(L, s, A.k);
   if (ws.e < 0) return;  // slot past the active experts
-  item_gateup_wide<BITS, kWideTM, SPLIT, kRoutedNI<BITS, SPLIT>>(A, Slot{nullptr, ws.e, ws.p0, ws.ne, ws.tokv}, j);
+  item_gateup_wide<BITS, kWideTM, SPLIT, NI>(A, Slot{nullptr, ws.e, ws.p0, ws.ne, ws.tokv}, j);
 }
 
-template <int BITS, bool SPLIT, bool YBF16, int EPL>
+template <int BITS, bool SPLIT, bool YBF16, int EPL, int NI = kRoutedNI<BITS, SPLIT>>
 moe_status launch_wide_routed(DecodeArgs& a, const RouteOut& r, int max_active, hipStream_t s) {
-  a.TA = (int)ceil_div(a.I, 4 * kRoutedNI<BITS, SPLIT>);
-  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_route_gateup_kernel<BITS, SPLIT, EPL>,
+  a.TA = (int)ceil_div(a.I, 4 * NI);
+  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_route_gateup_kernel<BITS, SPLIT, EPL, NI>,
            dim3((unsigned)(1 + max_active * a.TA)), dim3(256), 0, s, a, r);
   if (moe_status st = check_launch("ffn_route_gateup")) return st;
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
@@ -1118,8 +1118,17 @@ moe_status launch_wide_routed(DecodeArgs& a, const RouteOut& r, int max_active, 
   return check_launch("ffn_down");
 }
 
+// Four to six tokens (a verify step with three to five drafts) run 2-bit bf16
+// steps with four I rows per wave: twice the workgroups, half the rows each,
+// so the passes over an expert's tokens take half as long.  The rows' bits do
+// not depend on the rows per wave.
+#ifndef MOE_ROUTED_MID_T
+#define MOE_ROUTED_MID_T 1
+#endif
 template <bool SPLIT, bool YBF16, int EPL>
 moe_status launch_routed_b(DecodeArgs& a, const RouteOut& r, int bits, int max_active, hipStream_t s) {
+  if (MOE_ROUTED_MID_T && bits == 2 && !SPLIT && a.T >= 4 && a.T <= 6)
+    return launch_wide_routed<2, SPLIT, YBF16, EPL, 4>(a, r, max_active, s);
   return bits == 2   ? launch_wide_routed<2, SPLIT, YBF16, EPL>(a, r, max_active, s)
          : bits == 3 ? launch_wide_routed<3, SPLIT, YBF16, EPL>(a, r, max_active, s)
                      : launch_wide_routed<4, SPLIT, YBF16, EPL>(a, r, max_active, s);

@@ -269,12 +269,18 @@ def _assert_bit_identical(a, b, n):
     assert np.array_equal(to_host(o_a).view(np.uint32), to_host(o_b).view(np.uint32))
 
 
-@pytest.mark.parametrize("case", ["tiny", "decode_verify", "sweep1", "sweep2", "sweep4", "sweep8"])
+@pytest.mark.parametrize("case", ["tiny", "decode_verify", "verify4", "verify6", "sweep1", "sweep2", "sweep4",
+                                  "sweep8"])
 def test_layer_decode_bit_identical_to_four_calls(moe, case):
     if case == "tiny":
         w = synth.tiny()
         lg = w.logits()
         ex = w.experts()
+    elif case.startswith("verify"):  # 2-bit, bf16 x, four or six tokens: the four-rows-per-wave routed kernel
+        w = synth.Workload(f"verify_T{case[6:]}", E=512, k=10, H=2048, I=512, T=int(case[6:]), bits=2,
+                           x_dtype="bf16", zipf_s=1.1)
+        lg = w.logits()
+        ex = routed_experts(w, lg)
     else:
         w = synth.decode_verify() if case == "decode_verify" else synth.decode_sweep(int(case[5:]))
         lg = w.logits()
