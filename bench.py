@@ -54,8 +54,8 @@ BF16_PEAK_TFLOPS = 2500.0
 FETCH_SCALE = 262144.0 / 131093.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "8f6a01f8fbc49b43",
-                    "fetch_kib": 7632.2, "write_kib": 62.9},
+    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "c5bc2e0bf4ec1753",
+                    "fetch_kib": 7627.6, "write_kib": 62.9},
     "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "d4fdb911b67e081d", "fetch_kib": 297229.0,
                     "write_kib": 83621.0},
 }
