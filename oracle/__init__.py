@@ -23,7 +23,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", _SRC, "-o", tmp,
-                               "-lm"])
+                               "-lm", "-lpthread"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -56,6 +56,8 @@ def lib():
         L.oracle_router_logits.argtypes = [vp, i32, vp, i32, i32, i32, vp]
         L.oracle_layer.restype = i32
         L.oracle_layer.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_layer_mt.restype = i32
+        L.oracle_layer_mt.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -168,10 +170,19 @@ def router_logits(x: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
     return out
 
 
+def default_threads() -> int:
+    """Threads for oracle_layer_mt: OMP_NUM_THREADS when set, else the CPU count, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
 def layer(x: np.ndarray, logits: np.ndarray, experts: np.ndarray, k: int, H: int, I: int, bits: int,
-          residual: np.ndarray | None = None, want_y: bool = True) -> dict:
+          residual: np.ndarray | None = None, want_y: bool = True, nthreads: int = 1) -> dict:
     """Whole layer.  x: float32 [T,H] values or uint16 [T,H] raw bf16 bits.
-    experts: uint8 [E, stride] (expert e's blob in row e)."""
+    experts: uint8 [E, stride] (expert e's blob in row e).
+    nthreads > 1 runs oracle_layer_mt (same functions on the same rows, so the
+    same bits); nthreads = 1 runs oracle_layer."""
     x = np.ascontiguousarray(x)
     if x.dtype == np.uint16:
         xb = 1
@@ -190,8 +201,12 @@ def layer(x: np.ndarray, logits: np.ndarray, experts: np.ndarray, k: int, H: int
     y = np.empty((T, k, H), np.float64) if want_y else None
     out = np.empty((T, H), np.float64)
     r = None if residual is None else np.ascontiguousarray(residual, np.float64)
-    rc = lib().oracle_layer(_p(x), xb, _p(lg), _p(experts), stride, T, E, k, H, I, bits, _p(r), _p(ids), _p(w),
-                            _p(y), _p(out))
+    if nthreads > 1:
+        rc = lib().oracle_layer_mt(_p(x), xb, _p(lg), _p(experts), stride, T, E, k, H, I, bits, _p(r), _p(ids),
+                                   _p(w), _p(y), _p(out), int(nthreads))
+    else:
+        rc = lib().oracle_layer(_p(x), xb, _p(lg), _p(experts), stride, T, E, k, H, I, bits, _p(r), _p(ids), _p(w),
+                                _p(y), _p(out))
     if rc != 0:
         raise ValueError("oracle_layer: bad arguments")
     return {"ids": ids, "w": w, "y": y, "out": out}

@@ -44,6 +44,7 @@
  *   last plane rounded up to a multiple of 256.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -328,4 +329,193 @@ int oracle_layer(const void* x, int x_is_bf16, const float* logits, const uint8_
   free(wu);
   free(wg);
   return 0;
+}
+
+/* ---- the same layer on several threads (full-size checks and CPU timing) ---- */
+
+/* oracle_layer_mt computes what oracle_layer computes, with the same
+ * functions applied to the same rows, so its outputs equal oracle_layer's bit
+ * for bit whatever the thread count.  Only the order in which independent
+ * rows are visited changes:
+ *   1. routing: oracle_route on disjoint slices of tokens;
+ *   2. experts: work items of (expert, up to MT_ROWS of its assignments in
+ *      ascending order); each item decodes its expert with
+ *      oracle_dequant_matrix and runs oracle_ffn_decoded on each of its rows;
+ *      threads take items from a shared counter;
+ *   3. combine: oracle_combine on disjoint slices of tokens.
+ * y may be NULL.  Returns 0, or -1 on bad arguments or memory exhaustion. */
+
+#define MT_ROWS 256
+
+typedef struct {
+  /* shared inputs */
+  const void* x;
+  int x_is_bf16;
+  const float* logits;
+  const uint8_t* experts;
+  int64_t stride;
+  int T, E, k, H, I, bits, nthreads;
+  const double* residual;
+  /* shared outputs and schedule */
+  int32_t* ids;
+  double* w;
+  double* yall;
+  double* out;
+  const int32_t* order;  /* assignments grouped by expert, ascending inside */
+  const int64_t* item_first;
+  const int32_t* item_count;
+  int64_t n_items;
+  int64_t next_item;
+  int failed;
+} mt_job;
+
+typedef struct {
+  mt_job* job;
+  int rank;
+} mt_arg;
+
+static void mt_slice(int T, int nthreads, int rank, int* t0, int* t1) {
+  *t0 = (int)((int64_t)T * rank / nthreads);
+  *t1 = (int)((int64_t)T * (rank + 1) / nthreads);
+}
+
+static void* mt_route(void* p) {
+  mt_arg* a = (mt_arg*)p;
+  mt_job* j = a->job;
+  int t0, t1;
+  mt_slice(j->T, j->nthreads, a->rank, &t0, &t1);
+  if (t1 > t0 && oracle_route(j->logits + (int64_t)t0 * j->E, t1 - t0, j->E, j->k, j->ids + (int64_t)t0 * j->k,
+                              j->w + (int64_t)t0 * j->k) != 0)
+    j->failed = 1;
+  return NULL;
+}
+
+static void* mt_ffn(void* p) {
+  mt_arg* a = (mt_arg*)p;
+  mt_job* j = a->job;
+  size_t n = (size_t)j->H * (size_t)j->I;
+  double* wg = (double*)malloc(sizeof(double) * n);
+  double* wu = (double*)malloc(sizeof(double) * n);
+  double* wd = (double*)malloc(sizeof(double) * n);
+  double* xr = (double*)malloc(sizeof(double) * (size_t)j->H);
+  if (!wg || !wu || !wd || !xr) {
+    j->failed = 1;
+  } else {
+    for (;;) {
+      int64_t it = __atomic_fetch_add(&j->next_item, 1, __ATOMIC_RELAXED);
+      if (it >= j->n_items) break;
+      const int32_t* rows = j->order + j->item_first[it];
+      int e = j->ids[rows[0]];
+      const uint8_t* blob = j->experts + (int64_t)e * j->stride;
+      oracle_dequant_matrix(blob, j->H, j->I, j->bits, 0, wg);
+      oracle_dequant_matrix(blob, j->H, j->I, j->bits, 1, wu);
+      oracle_dequant_matrix(blob, j->H, j->I, j->bits, 2, wd);
+      for (int r = 0; r < j->item_count[it]; ++r) {
+        int64_t asg = rows[r], t = asg / j->k;
+        for (int c = 0; c < j->H; ++c) xr[c] = x_value(j->x, j->x_is_bf16, t * j->H + c);
+        oracle_ffn_decoded(wg, wu, wd, j->H, j->I, xr, NULL, j->yall + asg * j->H);
+      }
+    }
+  }
+  free(xr);
+  free(wd);
+  free(wu);
+  free(wg);
+  return NULL;
+}
+
+static void* mt_combine(void* p) {
+  mt_arg* a = (mt_arg*)p;
+  mt_job* j = a->job;
+  int t0, t1;
+  mt_slice(j->T, j->nthreads, a->rank, &t0, &t1);
+  if (t1 > t0)
+    oracle_combine(j->yall + (int64_t)t0 * j->k * j->H, j->w + (int64_t)t0 * j->k, t1 - t0, j->k, j->H,
+                   j->residual ? j->residual + (int64_t)t0 * j->H : NULL, j->out + (int64_t)t0 * j->H);
+  return NULL;
+}
+
+static int mt_run(mt_job* j, void* (*fn)(void*)) {
+  pthread_t th[256];
+  mt_arg args[256];
+  int started = 0;
+  for (int r = 0; r < j->nthreads; ++r) {
+    args[r].job = j;
+    args[r].rank = r;
+    if (r == 0) continue;
+    if (pthread_create(&th[r], NULL, fn, &args[r]) != 0) break;
+    started = r;
+  }
+  if (started < j->nthreads - 1) {
+    /* fewer threads than asked: the started ones and this one share the work
+     * only where the work is a shared queue; slices need every rank */
+    j->failed = 1;
+  }
+  fn(&args[0]);
+  for (int r = 1; r <= started; ++r) pthread_join(th[r], NULL);
+  return j->failed ? -1 : 0;
+}
+
+int oracle_layer_mt(const void* x, int x_is_bf16, const float* logits, const uint8_t* experts, int64_t stride, int T,
+                    int E, int k, int H, int I, int bits, const double* residual, int32_t* ids, double* w, double* y,
+                    double* out, int nthreads) {
+  if (H % 32 || I % 32 || bits < 2 || bits > 4 || T < 0 || E < 1 || k < 1 || k > E) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  const int64_t n = (int64_t)T * k;
+  mt_job j;
+  memset(&j, 0, sizeof j);
+  j.x = x;
+  j.x_is_bf16 = x_is_bf16;
+  j.logits = logits;
+  j.experts = experts;
+  j.stride = stride;
+  j.T = T;
+  j.E = E;
+  j.k = k;
+  j.H = H;
+  j.I = I;
+  j.bits = bits;
+  j.nthreads = nthreads;
+  j.residual = residual;
+  j.ids = ids;
+  j.w = w;
+  j.out = out;
+  if (mt_run(&j, mt_route) != 0) return -1;
+  /* group the assignments by expert (ascending inside) and cut the groups into items */
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n + 1));
+  int64_t* count = (int64_t*)calloc((size_t)E + 1, sizeof(int64_t));
+  int64_t* item_first = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n / MT_ROWS + E + 1));
+  int32_t* item_count = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n / MT_ROWS + E + 1));
+  double* yall = y ? y : (double*)malloc(sizeof(double) * ((size_t)n * (size_t)H + 1));
+  int rc = -1;
+  if (order && count && item_first && item_count && yall) {
+    for (int64_t a = 0; a < n; ++a) ++count[ids[a] + 1];
+    for (int e = 0; e < E; ++e) count[e + 1] += count[e];
+    int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+    if (fill) {
+      memcpy(fill, count, sizeof(int64_t) * (size_t)E);
+      for (int64_t a = 0; a < n; ++a) order[fill[ids[a]]++] = (int32_t)a;
+      free(fill);
+      int64_t ni = 0;
+      for (int e = 0; e < E; ++e)
+        for (int64_t p = count[e]; p < count[e + 1]; p += MT_ROWS) {
+          item_first[ni] = p;
+          item_count[ni] = (int32_t)((count[e + 1] - p) < MT_ROWS ? (count[e + 1] - p) : MT_ROWS);
+          ++ni;
+        }
+      j.order = order;
+      j.item_first = item_first;
+      j.item_count = item_count;
+      j.n_items = ni;
+      j.yall = yall;
+      if (mt_run(&j, mt_ffn) == 0 && mt_run(&j, mt_combine) == 0) rc = 0;
+    }
+  }
+  if (!y) free(yall);
+  free(item_count);
+  free(item_first);
+  free(count);
+  free(order);
+  return rc;
 }

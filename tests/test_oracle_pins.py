@@ -406,3 +406,21 @@ def test_router_bf16_tokens_decode_like_float32():
     xf = (xb.astype(np.uint32) << 16).view(np.float32)
     wr = synth.normal_bf16_bits(synth.stream_key(4, synth.TAG_ROUTER, 0), (10, 64))
     assert np.array_equal(oracle.router_logits(xb, wr), oracle.router_logits(xf, wr))
+
+
+# ---- the threaded driver --------------------------------------------------------
+
+@pytest.mark.parametrize("nthreads", [2, 3, 8])
+def test_threaded_layer_equals_single_thread_bit_for_bit(nthreads):
+    # E = 3, k = 2, T = 450: every expert gets more rows than one work item
+    # holds (256), so items of one expert are split across threads
+    w = synth.Workload("mt", E=3, k=2, H=64, I=32, T=450, bits=3, x_dtype="bf16", zipf_s=0.0, seed=4)
+    x, lg, ex = w.x(), w.logits(), w.experts()
+    res = np.random.default_rng(1).standard_normal((w.T, w.H))
+    one = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits, residual=res)
+    assert np.bincount(one["ids"].reshape(-1), minlength=w.E).min() > 256
+    many = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits, residual=res, nthreads=nthreads)
+    for key in ("ids", "w", "y", "out"):
+        assert np.array_equal(one[key], many[key]), key
+    no_y = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits, residual=res, nthreads=nthreads, want_y=False)
+    assert np.array_equal(one["out"], no_y["out"])
