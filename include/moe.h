@@ -79,7 +79,9 @@ typedef enum moe_status {
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Which expert-FFN kernels to run.  AUTO picks GEMV for T * k <= 128 routed rows
- * and MFMA above (the measured crossover on the 512-expert, top-10 decode layer). */
+ * and MFMA above (the measured crossover on the 512-expert, top-10 decode layer);
+ * the arithmetic, and with it the tolerance a caller can expect (about 1e-5
+ * against 5e-3 of a row's largest output), changes with the path. */
 typedef enum moe_ffn_path {
   MOE_PATH_AUTO = 0,
   MOE_PATH_GEMV = 1, /* fused dequant-GEMV, fp32 throughout: decode and verify steps */
@@ -177,7 +179,13 @@ moe_status moe_dispatch(const int32_t* ids, int T, int k, int E, int32_t* offset
  *   path     MOE_PATH_GEMV keeps g, u, h and the sums in fp32 (the bf16 dot
  *            instructions see x exactly, and fp32 values as a sum of two bf16
  *            parts); MOE_PATH_MFMA rounds the decoded weights, x and h to fp16
- *            (saturating at +-65504) and accumulates in fp32.
+ *            and accumulates in fp32.  It first scales each token row of x by
+ *            a power of two so that its largest magnitude lies in [1, 2), keeps
+ *            h scaled by the square of its token's factor and undoes both after
+ *            accumulation, so the fp16 range does not limit x or h; an h value
+ *            still beyond +-65504 after that scaling saturates and is counted:
+ *            once the call has completed, the first 4 bytes of ws hold that
+ *            count as a uint32 (0 when nothing saturated).
  *   ws       device scratch of at least moe_expert_ffn_workspace_bytes(...) bytes.
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE.
  */
