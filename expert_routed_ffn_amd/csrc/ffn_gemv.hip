@@ -1022,10 +1022,14 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t* __restr
 }
 
 // The wide kernels apply when gate/up rows split over 64 lanes and down rows
-// over 16 lanes in whole 32-column chunks.  One compiled instantiation serves
-// every T (passes of up to kWideTM rows): separately compiled copies of the
-// same pass were seen to round differently, and a token's row must not depend
-// on which other tokens share its step.
+// over 16 lanes in whole 32-column chunks.  Within one entry point one compiled
+// pass routine (passes of up to kWideTM rows) serves every T, so a token's row
+// does not depend on which other tokens share its step.  Separately compiled
+// copies of a pass rounded differently while the compiler chose the fused
+// multiply-adds; with contraction off and every FMA written out, the per-row
+// arithmetic is the same in every instantiation, which is what lets the 2-bit
+// steps of 4 to 6 tokens take a kernel with four I rows per wave (tested bit
+// for bit against the four-call step at T = 4, 5 and 6).
 bool wide_shape(int H, int I) { return H % 2048 == 0 && I % 512 == 0; }
 
 template <int BITS, bool SPLIT, bool YBF16>

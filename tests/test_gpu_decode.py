@@ -269,7 +269,7 @@ def _assert_bit_identical(a, b, n):
     assert np.array_equal(to_host(o_a).view(np.uint32), to_host(o_b).view(np.uint32))
 
 
-@pytest.mark.parametrize("case", ["tiny", "decode_verify", "verify4", "verify6", "sweep1", "sweep2", "sweep4",
+@pytest.mark.parametrize("case", ["tiny", "decode_verify", "verify4", "verify5", "verify6", "sweep1", "sweep2", "sweep4",
                                   "sweep8"])
 def test_layer_decode_bit_identical_to_four_calls(moe, case):
     if case == "tiny":

@@ -2,8 +2,10 @@
 
 The MFMA path rounds decoded weights, x and h to fp16, so outputs are compared
 with PREFILL_TOL in the per-row metric max|d| / max|ref|.  At the 8,192-token
-size the oracle computes a seeded sample of token rows one by one (rows are
-independent); smaller cases with ragged tiles are compared in full.
+size the oracle (on all host threads) checks every row of the 2-bit chunk on
+both routings, and for 3- and 4-bit codes one row in every (expert, M-tile)
+plus all rows against the GEMV path; smaller cases with ragged tiles are
+compared in full.
 """
 import numpy as np
 import pytest
@@ -35,40 +37,89 @@ def _run(moe, w, x, lg, ex, path="mfma", y_dtype=None):
     return ids, wt, d, y, out
 
 
-@pytest.fixture(scope="module")
-def prefill_experts():
-    return synth.prefill().experts(nthreads=synth.default_threads())
+_EXPERTS = {}
 
 
-@pytest.mark.parametrize("bias_scale,y_bf16", [(1.0, True), (0.21, False)])
-def test_prefill_8192_sampled_rows(moe, prefill_experts, bias_scale, y_bf16):
-    import torch
-    w = synth.prefill(bias_scale)
-    x, lg = w.x(), w.logits()
-    ids, wt, d, y, out = _run(moe, w, x, lg, prefill_experts, y_dtype=torch.bfloat16 if y_bf16 else torch.float32)
+def _experts(bits):
+    """All 512 experts of the prefill layer at `bits` (generated once per module)."""
+    if bits not in _EXPERTS:
+        _EXPERTS[bits] = synth.prefill(1.0, bits).experts(nthreads=synth.default_threads())
+    return _EXPERTS[bits]
+
+
+def _check_routing(moe, w, lg, ids, d):
     ids_h = to_host(ids)
     ref_ids, _ = oracle.route(lg, w.k)
     assert np.array_equal(ids_h, ref_ids)
+    ref_d = oracle.dispatch(ref_ids, w.E)
+    assert np.array_equal(to_host(d.offsets), ref_d["offsets"])
+    assert np.array_equal(to_host(d.sorted_assign)[:w.T * w.k], ref_d["sorted_assign"])
     counts = np.bincount(ids_h.reshape(-1), minlength=w.E)
     print(f"{w.name}: experts hit {int((counts > 0).sum())}, max rows {counts.max()}, min nonzero "
           f"{counts[counts > 0].min()}")
+    return ref_d
+
+
+@pytest.mark.parametrize("bias_scale,y_bf16", [(1.0, True), (0.21, False)])
+def test_prefill_8192_all_rows(moe, bias_scale, y_bf16):
+    """The 8,192-token chunk in the benchmark's launch configuration (four calls, MFMA path): every one of the
+    8,192 output rows and 81,920 expert rows against the oracle, run on all host threads."""
+    import torch
+    w = synth.prefill(bias_scale)
+    ex = _experts(2)
+    x, lg = w.x(), w.logits()
+    ids, wt, d, y, out = _run(moe, w, x, lg, ex, y_dtype=torch.bfloat16 if y_bf16 else torch.float32)
+    _check_routing(moe, w, lg, ids, d)
     out_h = to_host(out)
-    assert np.all(np.isfinite(out_h))
-    rng = np.random.default_rng(11)
-    sample = np.sort(rng.choice(w.T, size=40, replace=False))
-    # include rows of the most and least loaded experts
-    hot = int(np.argmax(counts))
-    sample = np.unique(np.concatenate([sample, np.nonzero((ids_h == hot).any(axis=1))[0][:4],
-                                       np.nonzero((ids_h == np.argmin(np.where(counts > 0, counts, 1 << 30))).any(axis=1))[0][:2]]))
-    ref = oracle.layer(x[sample], lg[sample], prefill_experts, w.k, w.H, w.I, w.bits)
     y_h = to_host(y)
-    ey = row_rel_err(y_h[sample], ref["y"])
-    eo = row_rel_err(out_h[sample], ref["out"])
-    print(f"{w.name}: sampled {len(sample)} rows, y err {ey:.3e}, out err {eo:.3e}")
+    del y
+    ref = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits, nthreads=oracle.default_threads())
+    eo = row_rel_err(out_h, ref["out"])
+    ey = row_rel_err(y_h, ref["y"])
+    print(f"{w.name}: all {w.T} rows: out err {eo:.3e}; all {w.T * w.k} expert rows: y err {ey:.3e}")
     # the layer output carries the path's tolerance; bf16 y rows carry one more
     # round-to-nearest (at most 2^-9 of the row's largest value)
     assert eo <= PREFILL_TOL
     assert ey <= PREFILL_TOL + (2.0 ** -9 if y_bf16 else 0.0)
+
+
+def _tile_rows(ref_d, k, bm=128, seed=0):
+    """Tokens such that every (expert, M-tile of bm sorted rows) holds at least one of their assignments.
+    Both GEMMs run on the same M-tiles.  Returns (tokens, number of tiles)."""
+    rng = np.random.default_rng(seed)
+    off, sa = ref_d["offsets"], ref_d["sorted_assign"]
+    toks, tiles = set(), 0
+    for e in range(len(off) - 1):
+        for p0 in range(int(off[e]), int(off[e + 1]), bm):
+            p1 = min(p0 + bm, int(off[e + 1]))
+            toks.add(int(sa[int(rng.integers(p0, p1))]) // k)
+            tiles += 1
+    return np.array(sorted(toks)), tiles
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bias_scale", [1.0, 0.21])
+def test_prefill_8192_low_bit_every_tile(moe, bits, bias_scale):
+    """3- and 4-bit chunks: one checked row in every (expert, M-tile) against the oracle, and all 8,192 rows
+    against the GEMV path (fp32 throughout, oracle-checked at 2e-3) on the same inputs."""
+    w = synth.prefill(bias_scale, bits)
+    ex = _experts(bits)
+    x, lg = w.x(), w.logits()
+    ids, wt, d, y, out = _run(moe, w, x, lg, ex)
+    ref_d = _check_routing(moe, w, lg, ids, d)
+    out_h = to_host(out)
+    y_h = to_host(y)
+    del y, out
+    toks, tiles = _tile_rows(ref_d, w.k)
+    ref = oracle.layer(x[toks], lg[toks], ex, w.k, w.H, w.I, w.bits, nthreads=oracle.default_threads())
+    eo = row_rel_err(out_h[toks], ref["out"])
+    ey = row_rel_err(y_h[toks], ref["y"])
+    del y_h
+    g = _run(moe, w, x, lg, ex, path="gemv")
+    eg = row_rel_err(out_h, to_host(g[4]))
+    print(f"{w.name}: {tiles} M-tiles covered by {len(toks)} checked tokens: out err {eo:.3e}, y err {ey:.3e}; "
+          f"all {w.T} rows against the GEMV path: {eg:.3e}")
+    assert eo <= PREFILL_TOL and ey <= PREFILL_TOL and eg <= PREFILL_TOL
 
 
 def _custom(E, k, H, I, T, bits, x_dtype="bf16", zipf=0.0, seed=5):
@@ -114,3 +165,66 @@ def test_mfma_is_deterministic(moe):
     a = _run(moe, w, x, lg, ex)
     b = _run(moe, w, x, lg, ex)
     assert np.array_equal(to_host(a[3]), to_host(b[3])) and np.array_equal(to_host(a[4]), to_host(b[4]))
+
+
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16)).astype(np.uint16)
+
+
+def _clip_count(ws) -> int:
+    return int(ws[:4].cpu().numpy().view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_mfma_rows_far_outside_fp16_range(moe, sign):
+    """Token rows scaled by 10^(sign * (t mod 7)): magnitudes up to 1e6 (h up to about 1e11) or down to 1e-6.
+    The per-row power-of-two scaling keeps every row within the path's tolerance, with nothing saturated."""
+    import torch
+    w = _custom(16, 4, 256, 128, 200, 2, "bf16", 0.5, seed=8)
+    xb = w.x()
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    scale = (10.0 ** (sign * (np.arange(w.T) % 7))).astype(np.float32)[:, None]
+    x = _bf16_bits(xf * scale)
+    lg, ex = w.logits(), w.experts()
+    layer = moe.ExpertLayer(w.E, w.H, w.I, w.bits, to_dev(ex))
+    ws = torch.zeros(layer.workspace_bytes(w.T, w.k, "mfma"), dtype=torch.uint8, device="cuda")
+    ids, wt, d, y, out = moe.layer_forward(layer, to_dev_x(x), to_dev(lg), w.k, path="mfma", bufs={"ws": ws})
+    torch.cuda.synchronize()
+    ref = oracle.layer(x, lg, ex, w.k, w.H, w.I, w.bits)
+    assert np.array_equal(to_host(ids), ref["ids"])
+    ey, eo = row_rel_err(to_host(y), ref["y"]), row_rel_err(to_host(out), ref["out"])
+    print(f"rows scaled up to 1e{6 * sign}: largest |out| {np.abs(ref['out']).max():.3e}, y err {ey:.3e}, "
+          f"out err {eo:.3e}, saturated {_clip_count(ws)}")
+    assert ey <= PREFILL_TOL and eo <= PREFILL_TOL
+    assert _clip_count(ws) == 0
+
+
+def test_mfma_saturation_is_counted(moe):
+    """Weights with rows of L1 norm near 1e5 push h beyond the fp16 range even after the row scaling: the values
+    saturate and the first word of the workspace counts them (it is cleared by every call)."""
+    import torch
+    from tests import _blob
+    E, k, H, I, T, bits = 2, 1, 64, 32, 160, 2
+    big = _blob.build_blob(H, I, bits, [_blob.constant_matrix(I, H, 3, 512.0, 0.0),
+                                        _blob.constant_matrix(I, H, 3, 512.0, 0.0),
+                                        _blob.constant_matrix(H, I, 1, 1.0, 0.0)])
+    small = _blob.build_blob(H, I, bits, [_blob.constant_matrix(I, H, 1, 2.0 ** -10, 0.0),
+                                          _blob.constant_matrix(I, H, 1, 2.0 ** -10, 0.0),
+                                          _blob.constant_matrix(H, I, 1, 1.0, 0.0)])
+    ex = np.stack([big, small])
+    x = np.abs(np.random.default_rng(3).standard_normal((T, H))).astype(np.float32) + 0.5
+    x_d = torch.from_numpy(x).cuda()
+    ws = torch.zeros(moe.ExpertLayer(E, H, I, bits, to_dev(ex)).workspace_bytes(T, k, "mfma"), dtype=torch.uint8,
+                     device="cuda")
+    layer = moe.ExpertLayer(E, H, I, bits, to_dev(ex))
+    to_big = np.tile(np.array([[1.0, 0.0]], np.float32), (T, 1))
+    moe.layer_forward(layer, x_d, to_dev(to_big), k, path="mfma", bufs={"ws": ws})
+    torch.cuda.synchronize()
+    assert _clip_count(ws) == T * I  # g' = u' = 1536 * sum(x') > 2^8, so every h' = g' u' > 65504
+    to_small = np.tile(np.array([[0.0, 1.0]], np.float32), (T, 1))
+    ids, wt, d, y, out = moe.layer_forward(layer, x_d, to_dev(to_small), k, path="mfma", bufs={"ws": ws})
+    torch.cuda.synchronize()
+    assert _clip_count(ws) == 0
+    ref = oracle.layer(x, to_small, ex, k, H, I, bits)
+    assert row_rel_err(to_host(out), ref["out"]) <= PREFILL_TOL

@@ -3,8 +3,9 @@
 A small chained stack (layers feed each other through combine's residual and
 bf16 output) runs once with every expert resident in device memory and once
 through a slot table holding only part of them, misses copied from
-page-locked host memory; every layer's outputs must be bit-identical.  The
-stack's first layer is also checked against the oracle.
+page-locked host memory; every layer's outputs must be bit-identical.  Every
+layer output of the slot-table runs is also checked against the oracle on the
+same input bytes (each layer's bf16 input, its logits and its master blobs).
 """
 import numpy as np
 import pytest
@@ -38,8 +39,30 @@ def _host_master(w, torch):
     return host
 
 
-def _run(moe, torch, w, layer_of, steps, resolve=None):
-    """Run `steps` decode steps through the stack; returns every layer's (y, out) per step."""
+DECODE_TOL = 2e-3
+
+
+def _bf16_to_f64(bits_u16):
+    return (np.asarray(bits_u16, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _check_against_oracle(w, host, cases):
+    """cases: (layer, x as raw bf16 bits or fp32 values, logits, layer output with x as residual).
+    The oracle runs each layer on the same bytes; the per-row error of out - x is held to DECODE_TOL."""
+    ex_all = host.numpy().reshape(w.layers, w.E, w.expert_bytes)
+    worst = 0.0
+    for l, x_np, lg_np, out in cases:
+        res = _bf16_to_f64(x_np) if x_np.dtype == np.uint16 else x_np.astype(np.float64)
+        ref = oracle.layer(x_np, lg_np, ex_all[l], w.k, w.H, w.I, w.bits, residual=res, want_y=False,
+                           nthreads=oracle.default_threads())
+        worst = max(worst, row_rel_err(out - res, ref["out"] - res))
+    print(f"{len(cases)} layer steps against the oracle: max row error {worst:.3e}")
+    assert worst <= DECODE_TOL
+
+
+def _run(moe, torch, w, layer_of, steps, resolve=None, record=None):
+    """Run `steps` decode steps through the stack; returns every layer's (y, out) per step.
+    With `record` (a list), appends (layer, x bits, logits, out) of every layer step."""
     dev = torch.device("cuda")
     outs = []
     for s in range(steps):
@@ -57,6 +80,8 @@ def _run(moe, torch, w, layer_of, steps, resolve=None):
             out = moe.combine(y, wt, residual=x, out_bf16=nxt.view(torch.int16))
             torch.cuda.synchronize()
             outs.append((to_host(y).copy(), to_host(out).copy()))
+            if record is not None:
+                record.append((l, x.view(torch.int16).cpu().numpy().view(np.uint16).copy(), lg_np, outs[-1][1]))
             x = nxt
     return outs
 
@@ -80,8 +105,9 @@ def test_slot_table_matches_resident_bit_for_bit(moe, n_slots):
         order = np.argsort(-w.bias(l), kind="stable")[: n_slots // (2 * w.layers)]
         pairs += [(l, int(e)) for e in order]
     table.preload(pairs)
+    rec = []
     got = _run(moe, torch, w, lambda l: table.layer(l, w.H, w.I, w.bits), steps=4,
-               resolve=lambda l, d: table.resolve(l, d))
+               resolve=lambda l, d: table.resolve(l, d), record=rec)
     st = table.stats()
     table.close()
     assert st["misses"] > 0 and st["resolves"] == 4 * w.layers
@@ -89,24 +115,7 @@ def test_slot_table_matches_resident_bit_for_bit(moe, n_slots):
         assert st["evictions"] > 0
     for (ya, oa), (yb, ob) in zip(ref, got):
         assert np.array_equal(ya, yb) and np.array_equal(oa, ob)
-
-
-def test_stack_first_layer_matches_oracle(moe):
-    import torch
-    w = _stack()
-    host = _host_master(w, torch)
-    eb = w.expert_bytes
-    dev_all = host.to("cuda")
-    layer0 = moe.ExpertLayer(w.E, w.H, w.I, w.bits, dev_all, eb)
-    lg_np = synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, 0, 0), w.T, w.E, synth.drifted_bias(w, 0, 0, 0.05))
-    x_np = w.x(0, 0)
-    x = torch.from_numpy(x_np.view(np.int16).copy()).view(torch.bfloat16).cuda()
-    ids, wt, d, y, out = moe.layer_forward(layer0, x, to_dev(lg_np), w.k, residual=x, path="gemv")
-    ex = host.numpy().reshape(w.layers, w.E, eb)[0]
-    res = (x_np.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    ref = oracle.layer(x_np, lg_np, ex, w.k, w.H, w.I, w.bits, residual=res)
-    assert np.array_equal(to_host(ids), ref["ids"])
-    assert row_rel_err(to_host(out) - res, ref["out"] - res) <= 2e-3
+    _check_against_oracle(w, host, rec)
 
 
 def test_slot_table_rejects_pageable_host_memory(moe):
@@ -161,8 +170,9 @@ def test_slot_table_device_mode_matches_resident_bit_for_bit(moe, n_slots):
     table = moe.SlotTable(w.layers, w.E, n_slots, eb, host, slots, smap)
     table.preload(_warm_pairs(w, n_slots))
     table.enable_device()
+    rec = []
     got = _run(moe, torch, w, lambda l: table.layer(l, w.H, w.I, w.bits), steps=4,
-               resolve=lambda l, d: table.resolve_device(l, d))
+               resolve=lambda l, d: table.resolve_device(l, d), record=rec)
     st = table.stats()
     table.close()
     assert st["misses"] > 0 and st["resolves"] == 4 * w.layers
@@ -170,6 +180,7 @@ def test_slot_table_device_mode_matches_resident_bit_for_bit(moe, n_slots):
         assert st["evictions"] > 0
     for (ya, oa), (yb, ob) in zip(ref, got):
         assert np.array_equal(ya, yb) and np.array_equal(oa, ob)
+    _check_against_oracle(w, host, rec)
 
 
 def test_slot_table_device_policy_equals_host_policy(moe):
@@ -257,6 +268,7 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, bits, T, n_slots,
         t.enable_device()
         tables.append(t)
     fused, split = tables
+    rec = []
     for s in range(3):
         x = torch.from_numpy(w.x(0, s).view(np.int16).copy()).view(torch.bfloat16).cuda()
         for l in range(w.layers):
@@ -271,6 +283,8 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, bits, T, n_slots,
             torch.cuda.synchronize()
             for u, v in zip((a[0], a[1], a[3], a[4]), (b[0], b[1], b[3], b[4])):
                 assert np.array_equal(to_host(u).view(np.uint32), to_host(v).view(np.uint32)), (s, l)
+            x_np = x.cpu().numpy() if xf32 else x.view(torch.int16).cpu().numpy().view(np.uint16)
+            rec.append((l, x_np.copy(), to_host(lg).copy(), to_host(b[4]).copy()))
             x = a[4].to(torch.bfloat16)
     assert fused.stats() == split.stats()
     assert np.array_equal(fused.map_host(), split.map_host())
@@ -288,3 +302,4 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, bits, T, n_slots,
         assert np.array_equal(slots_h[sl * eb:(sl + 1) * eb], host_h[g * eb:(g + 1) * eb]), (g, sl)
     for t in tables:
         t.close()
+    _check_against_oracle(w, host, rec)
