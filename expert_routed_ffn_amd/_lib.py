@@ -133,6 +133,17 @@ def _stream(stream, device=None):
     return ctypes.c_void_p(int(stream))
 
 
+def _on(stream, device):
+    """Context in which the binding allocates outputs and workspaces: the stream the kernels run on, so the
+    caching allocator does not hand their memory to other work while the kernels are still queued."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return MOE_F32
@@ -172,10 +183,11 @@ def route_topk(logits: torch.Tensor, k: int, ids: torch.Tensor | None = None, w:
                stream=None):
     _need(logits, "logits")
     T, E = logits.shape
-    if ids is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-    if w is None:
-        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    with _on(stream, logits.device):
+        if ids is None:
+            ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        if w is None:
+            w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check(lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream, logits.device)))
     return ids, w
 
@@ -190,8 +202,9 @@ def router_logits(x: torch.Tensor, w_r: torch.Tensor, logits: torch.Tensor | Non
         raise TypeError("w_r must be bfloat16")
     T, H = x.shape
     E = w_r.shape[0]
-    if logits is None:
-        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    with _on(stream, x.device):
+        if logits is None:
+            logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     _check(lib.moe_router_logits(_ptr(x), _dtype_code(x), _ptr(w_r), T, H, E, _ptr(logits),
                                  _stream(stream, x.device)))
     return logits
@@ -205,12 +218,13 @@ def router_topk(x: torch.Tensor, w_r: torch.Tensor, k: int, logits: torch.Tensor
     T, H = x.shape
     E = w_r.shape[0]
     dev = x.device
-    if logits is None:
-        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    if ids is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    if w is None:
-        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    with _on(stream, dev):
+        if logits is None:
+            logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        if ids is None:
+            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        if w is None:
+            w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(lib.moe_router_topk(_ptr(x), _dtype_code(x), _ptr(w_r), T, H, E, k, _ptr(logits), _ptr(ids), _ptr(w),
                                _stream(stream, dev)))
     return logits, ids, w
@@ -236,7 +250,8 @@ class Dispatch:
 def dispatch(ids: torch.Tensor, E: int, out: Dispatch | None = None, stream=None) -> Dispatch:
     _need(ids, "ids")
     T, k = ids.shape
-    d = out if out is not None else Dispatch(T, k, E, ids.device)
+    with _on(stream, ids.device):
+        d = out if out is not None else Dispatch(T, k, E, ids.device)
     _check(lib.moe_dispatch(_ptr(ids), T, k, E, _ptr(d.offsets), _ptr(d.sorted_assign), _ptr(d.assign_pos),
                             _ptr(d.active), _ptr(d.n_active), _ptr(d.ws), d.ws.numel(), _stream(stream, ids.device)))
     return d
@@ -265,11 +280,12 @@ def expert_ffn_q(layer: ExpertLayer, x: torch.Tensor, k: int, d: Dispatch, y: to
                  y_dtype=torch.float32, path: str = "auto", ws: torch.Tensor | None = None, stream=None):
     _need(x, "x")
     T, H = x.shape
-    if y is None:
-        y = torch.empty((T, k, H), dtype=y_dtype, device=x.device)
+    with _on(stream, x.device):
+        if y is None:
+            y = torch.empty((T, k, H), dtype=y_dtype, device=x.device)
+        if ws is None:
+            ws = torch.empty(max(layer.workspace_bytes(T, k, path), 1), dtype=torch.uint8, device=x.device)
     _need(y, "y")
-    if ws is None:
-        ws = torch.empty(max(layer.workspace_bytes(T, k, path), 1), dtype=torch.uint8, device=x.device)
     _check(lib.moe_expert_ffn_q(ctypes.byref(layer.q), _ptr(x), _dtype_code(x), T, k, _ptr(d.offsets),
                                 _ptr(d.sorted_assign), _ptr(d.active), _ptr(d.n_active), _ptr(y), _dtype_code(y),
                                 PATHS[path], _ptr(ws), ws.numel(), _stream(stream, x.device)))
@@ -283,8 +299,9 @@ def combine(y: torch.Tensor, w: torch.Tensor, residual: torch.Tensor | None = No
     _need(y, "y")
     _need(w, "w")
     T, k, H = y.shape
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.float32, device=y.device)
+    with _on(stream, y.device):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.float32, device=y.device)
     r_t = MOE_F32 if residual is None else _dtype_code(residual)
     _check(lib.moe_combine(_ptr(y), _dtype_code(y), _ptr(w), T, k, H, _ptr(residual), r_t, _ptr(out),
                            _ptr(out_bf16), _stream(stream, y.device)))
@@ -309,6 +326,29 @@ def layer_forward(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: 
 
 # ---- fused decode step ------------------------------------------------------------
 
+def _decode_buffers(layer, T, k, H, y_dtype, b, stream, dev):
+    """Outputs and workspace of a decode step: the caller's from `b`, the rest allocated on `stream`."""
+    with _on(stream, dev):
+        ids = b.get("ids")
+        if ids is None:
+            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = b.get("w")
+        if w is None:
+            w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        d = b.get("dispatch") or Dispatch(T, k, layer.E, dev)
+        y = b.get("y")
+        if y is None:
+            y = torch.empty((T, k, H), dtype=y_dtype, device=dev)
+        out = b.get("out")
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = b.get("dws")
+        if ws is None:
+            ws = torch.empty(max(int(lib.moe_layer_decode_workspace_bytes(ctypes.byref(layer.q), T, k)), 1),
+                             dtype=torch.uint8, device=dev)
+    return ids, w, d, y, out, ws
+
+
 def layer_decode(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: int, residual=None,
                  y_dtype=torch.float32, out_bf16: torch.Tensor | None = None, bufs=None, stream=None):
     """moe_layer_decode: the whole layer step (two launches for the decode shapes, else four).  Returns (ids, w, dispatch, y, out)."""
@@ -316,24 +356,7 @@ def layer_decode(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: i
     _need(logits, "logits")
     T, H = x.shape
     dev = x.device
-    b = bufs or {}
-    ids = b.get("ids")
-    if ids is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = b.get("w")
-    if w is None:
-        w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    d = b.get("dispatch") or Dispatch(T, k, layer.E, dev)
-    y = b.get("y")
-    if y is None:
-        y = torch.empty((T, k, H), dtype=y_dtype, device=dev)
-    out = b.get("out")
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws = b.get("dws")
-    if ws is None:
-        ws = torch.empty(max(int(lib.moe_layer_decode_workspace_bytes(ctypes.byref(layer.q), T, k)), 1),
-                         dtype=torch.uint8, device=dev)
+    ids, w, d, y, out, ws = _decode_buffers(layer, T, k, H, y_dtype, bufs or {}, stream, dev)
     r_t = MOE_F32 if residual is None else _dtype_code(residual)
     _check(lib.moe_layer_decode(ctypes.byref(layer.q), _ptr(logits), _ptr(x), _dtype_code(x), T, k, _ptr(residual),
                                 r_t, _ptr(ids), _ptr(w), _ptr(d.offsets), _ptr(d.sorted_assign), _ptr(d.assign_pos),
@@ -350,24 +373,7 @@ def layer_decode_slots(table, l: int, layer: ExpertLayer, x: torch.Tensor, logit
     _need(logits, "logits")
     T, H = x.shape
     dev = x.device
-    b = bufs or {}
-    ids = b.get("ids")
-    if ids is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = b.get("w")
-    if w is None:
-        w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    d = b.get("dispatch") or Dispatch(T, k, layer.E, dev)
-    y = b.get("y")
-    if y is None:
-        y = torch.empty((T, k, H), dtype=y_dtype, device=dev)
-    out = b.get("out")
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws = b.get("dws")
-    if ws is None:
-        ws = torch.empty(max(int(lib.moe_layer_decode_workspace_bytes(ctypes.byref(layer.q), T, k)), 1),
-                         dtype=torch.uint8, device=dev)
+    ids, w, d, y, out, ws = _decode_buffers(layer, T, k, H, y_dtype, bufs or {}, stream, dev)
     r_t = MOE_F32 if residual is None else _dtype_code(residual)
     _check(lib.moe_layer_decode_slots(ctypes.byref(layer.q), table.h, l, _ptr(logits), _ptr(x), _dtype_code(x), T, k,
                                       _ptr(residual), r_t, _ptr(ids), _ptr(w), _ptr(d.offsets), _ptr(d.sorted_assign),
