@@ -5,10 +5,10 @@ include/moe.h); this package is its Python binding.
 """
 from ._lib import (MOE_BF16, MOE_F32, MOE_OK, Dispatch, ExpertLayer, HostSlotTable, MoeError, SlotTable, abi_version,
                    combine, decode_workspace_bytes, dispatch, expert_bytes, expert_ffn_q, header_functions,
-                   layer_decode, layer_decode_slots, layer_forward, lib,
+                   layer_decode, layer_decode_noalloc, layer_decode_slots, layer_forward, lib, noalloc_max_bytes,
                    profile_next_launch, route_topk, router_logits, router_topk)
 
 __all__ = ["MOE_BF16", "MOE_F32", "MOE_OK", "Dispatch", "ExpertLayer", "HostSlotTable", "MoeError", "SlotTable",
            "abi_version", "combine", "decode_workspace_bytes", "dispatch", "expert_bytes", "expert_ffn_q",
-           "header_functions", "layer_decode", "layer_decode_slots", "layer_forward", "lib",
-           "profile_next_launch", "route_topk", "router_logits", "router_topk"]
+           "header_functions", "layer_decode", "layer_decode_noalloc", "layer_decode_slots", "layer_forward", "lib",
+           "noalloc_max_bytes", "profile_next_launch", "route_topk", "router_logits", "router_topk"]

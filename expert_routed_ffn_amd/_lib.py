@@ -98,6 +98,11 @@ def _load():
     L.moe_layer_decode.restype = st
     L.moe_layer_decode.argtypes = [ctypes.POINTER(QLayer), vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                    vp, i32, vp, vp, vp, sz, vp]
+    L.moe_layer_decode_noalloc_max_bytes.restype = sz
+    L.moe_layer_decode_noalloc_max_bytes.argtypes = []
+    L.moe_layer_decode_noalloc.restype = st
+    L.moe_layer_decode_noalloc.argtypes = [ctypes.POINTER(QLayer), vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, i32, vp, vp, vp]
     L.moe_layer_decode_slots.restype = st
     L.moe_layer_decode_slots.argtypes = [ctypes.POINTER(QLayer), vp, i32, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp,
                                          vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
@@ -363,6 +368,29 @@ def layer_decode(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: i
                                 _ptr(d.active), _ptr(d.n_active), _ptr(y), _dtype_code(y), _ptr(out), _ptr(out_bf16),
                                 _ptr(ws), ws.numel(), _stream(stream, dev)))
     return ids, w, d, y, out
+
+
+def layer_decode_noalloc(layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: int, residual=None,
+                         y_dtype=torch.float32, out_bf16: torch.Tensor | None = None, bufs=None, stream=None):
+    """moe_layer_decode_noalloc: moe_layer_decode with the library's fixed device scratch as its workspace (no
+    workspace argument; outputs from `bufs` or allocated here).  Returns (ids, w, dispatch, y, out)."""
+    _need(x, "x")
+    _need(logits, "logits")
+    T, H = x.shape
+    dev = x.device
+    b = dict(bufs or {})
+    b["dws"] = torch.empty(0, dtype=torch.uint8, device=dev)  # unused: the call takes no workspace
+    ids, w, d, y, out, _ = _decode_buffers(layer, T, k, H, y_dtype, b, stream, dev)
+    r_t = MOE_F32 if residual is None else _dtype_code(residual)
+    _check(lib.moe_layer_decode_noalloc(ctypes.byref(layer.q), _ptr(logits), _ptr(x), _dtype_code(x), T, k,
+                                        _ptr(residual), r_t, _ptr(ids), _ptr(w), _ptr(d.offsets),
+                                        _ptr(d.sorted_assign), _ptr(d.assign_pos), _ptr(d.active), _ptr(d.n_active),
+                                        _ptr(y), _dtype_code(y), _ptr(out), _ptr(out_bf16), _stream(stream, dev)))
+    return ids, w, d, y, out
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib.moe_layer_decode_noalloc_max_bytes())
 
 
 def layer_decode_slots(table, l: int, layer: ExpertLayer, x: torch.Tensor, logits: torch.Tensor, k: int,

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["api.hip", "route_topk.hip", "dispatch.hip", "ffn_gemv.hip", "ffn_mfma.hip", "combine.hip",
-           "slot_table.hip", "router.hip"]
+           "slot_table.hip", "router.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code.  Floating-point

@@ -230,6 +230,29 @@ moe_status moe_layer_decode(const moe_qlayer* q, const float* logits, const void
                             hipStream_t stream);
 
 /*
+ * moe_layer_decode_noalloc -- moe_layer_decode without a caller workspace, for
+ * callers that cannot allocate device memory or pass one in (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation).  The workspace is a fixed array of
+ * moe_layer_decode_noalloc_max_bytes() bytes (1 MiB) in this library's device
+ * code, one per GPU, held until the process ends; the call allocates nothing.
+ * Steps whose moe_layer_decode_workspace_bytes exceeds it return
+ * MOE_EUNSUPPORTED (the 512-expert, top-10, 2048 x 512 layer needs about
+ * 0.2 MB at T = 3 and 0.8 MB at T = 12).  Arguments, outputs and errors are
+ * those of moe_layer_decode, whose kernels it runs, and every output is
+ * bit-identical to it.  All calls on one GPU share that GPU's array: calls
+ * that can overlap on one GPU (several streams, several host threads) race and
+ * must be ordered by the caller.  The first call on a device looks the array
+ * up with that device current.
+ */
+size_t moe_layer_decode_noalloc_max_bytes(void);
+moe_status moe_layer_decode_noalloc(const moe_qlayer* q, const float* logits, const void* x, moe_dtype x_t, int T,
+                                    int k, const void* residual, moe_dtype r_t, int32_t* ids, float* w,
+                                    int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, int32_t* active,
+                                    int32_t* n_active, void* y, moe_dtype y_t, float* out, uint16_t* out_bf16,
+                                    hipStream_t stream);
+
+/*
  * Resident-expert slot table.
  * Passage: the most-called experts stay resident in GPU memory while all of
  * them sit in host RAM; a routed expert that is resident is used at once and
