@@ -45,7 +45,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 (and bf16) MFMA, MI355X
+ROUNDS = 3  # timed rounds per measurement; the value is their median
 
 # Memory traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two runs), scaled
 # by what the same counters read for a plain 256 MiB device-to-device copy in the same runs (FETCH_SIZE reads
@@ -54,8 +55,6 @@ BF16_PEAK_TFLOPS = 2500.0
 FETCH_SCALE = 262144.0 / 131093.5
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp"], "sha": "c5bc2e0bf4ec1753",
-                    "fetch_kib": 7627.6, "write_kib": 62.9},
     "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "d4fdb911b67e081d", "fetch_kib": 297229.0,
                     "write_kib": 83621.0},
 }
@@ -181,10 +180,13 @@ def decode_bench(args, torch, moe, synth, oracle, bits: int = 2):
             step(i)
     g.replay()  # one untimed replay (graph upload)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    rounds = []
+    for _ in range(ROUNDS):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        rounds.append(time.perf_counter() - t0)
+    elapsed = sorted(rounds)[len(rounds) // 2]
     got2 = bufs["out"].cpu().numpy().astype(np.float64)
     if not np.array_equal(got, got2):
         raise SystemExit("bench: graph replay output differs from the eager step")
@@ -204,8 +206,8 @@ def decode_bench(args, torch, moe, synth, oracle, bits: int = 2):
     if not np.array_equal(got, bufs["out"].cpu().numpy().astype(np.float64)):
         raise SystemExit("bench: the four-call step differs from the fused step")
 
-    # dominant kernel: the gate/up GEMV (two thirds of the bytes); the down
-    # kernel is timed on alternate steps
+    # dominant kernel: the routed gate/up GEMV (routing + two thirds of the bytes); the down kernel (with the
+    # combine folded in) is timed on alternate steps; the first cycle of copies pays first-touch costs
     nprof = 2 * max(NL, 96)
     timer = KernelTimer(nprof)
     for i in range(nprof):
@@ -214,7 +216,6 @@ def decode_bench(args, torch, moe, synth, oracle, bits: int = 2):
     torch.cuda.synchronize()
     kt = timer.times_ms()
     timer.close()
-    # the first cycle of copies pays first-touch costs; use the rest
     gu = kt[0::2][NL:] if len(kt) // 2 > NL else kt[0::2]
     dn = kt[1::2][NL:] if len(kt) // 2 > NL else kt[1::2]
     gu_ms = sum(gu) / len(gu)
@@ -227,6 +228,8 @@ def decode_bench(args, torch, moe, synth, oracle, bits: int = 2):
     res = {
         "value": T * args.steps / elapsed,
         "ms_per_step": elapsed * 1e3 / args.steps,
+        "rounds_us_per_step": {"median": elapsed * 1e6 / args.steps, "min": min(rounds) * 1e6 / args.steps,
+                               "max": max(rounds) * 1e6 / args.steps, "n": len(rounds)},
         "U": U,
         "err": err,
         "gen_s": gen_s,
@@ -251,11 +254,12 @@ def decode_bench(args, torch, moe, synth, oracle, bits: int = 2):
     return res, (x_np, lg_np, ex, w)
 
 
-def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2):
+def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2, bias: float | None = None):
     """8,192-token prompt chunk through one layer (MFMA path)."""
     import numpy as np
 
-    w = synth.prefill(args.prefill_bias, bits)
+    bias = args.prefill_bias if bias is None else bias
+    w = synth.prefill(bias, bits)
     dev = torch.device("cuda:0")
     ex = w.experts(nthreads=synth.default_threads())
     x_np, lg_np = w.x(), w.logits()
@@ -305,12 +309,15 @@ def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2):
     torch.cuda.synchronize()
     if not torch.equal(bufs["out"], eager_out):
         raise SystemExit("bench: prefill graph replay differs from the eager step")
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    el = (time.perf_counter() - t0) / args.prefill_steps
-    if not torch.equal(bufs["out"], eager_out):
-        raise SystemExit("bench: prefill graph replay differs from the eager step")
+    rounds = []
+    for _ in range(ROUNDS):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        rounds.append((time.perf_counter() - t0) / args.prefill_steps)
+        if not torch.equal(bufs["out"], eager_out):
+            raise SystemExit("bench: prefill graph replay differs from the eager step")
+    el = sorted(rounds)[len(rounds) // 2]
     del g
 
     n = T * k
@@ -330,23 +337,28 @@ def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2):
     counts = np.bincount(bufs["ids"].cpu().numpy().reshape(-1), minlength=w.E)
     return {
         "workload": f"prefill chunk: T=8192, 512 experts, top-10, hidden 2048, intermediate 512, {bits}-bit, "
-                    f"Zipf({1.1 * args.prefill_bias:g}) router bias",
+                    f"Zipf({1.1 * bias:g}) router bias",
         "value": T / el,
         "unit": "tokens/s",
+        "dtype": "f16 MFMA (weights, x, h), f32 accumulation; bf16 y",
         "ms_per_step": el * 1e3,
+        "rounds_ms_per_step": {"median": el * 1e3, "min": min(rounds) * 1e3, "max": max(rounds) * 1e3,
+                               "n": len(rounds)},
         "hip_graph": True,
         "eager_ms_per_step": eager * 1e3,
         "layer_tflops": (gu_flops + dn_flops) / el / 1e12,
         "experts_hit": int((counts > 0).sum()),
         "max_rows_per_expert": int(counts.max()),
+        "min_rows_per_hit_expert": int(counts[counts > 0].min()),
         "sample_row_err": err,
+        "_data": (x_np, lg_np, ex, w),
         "roofline": {
             "bound": "mfma",
             "achieved": gu_flops / (gu_ms * 1e-3) / 1e12,
-            "peak": BF16_PEAK_TFLOPS,
+            "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "traffic": measured_traffic("mfma_gateup") if bits == 2 else None,
+            "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "traffic": measured_traffic("mfma_gateup") if bits == 2 and bias == 1.0 else None,
             "kernel": "mfma_ffn_kernel gate/up (fp16 MFMA, weights decoded in LDS)",
             "flops_per_launch": gu_flops,
             "mean_us": gu_ms * 1e3,
@@ -395,7 +407,7 @@ def router_bench(args, torch, moe, synth, oracle):
         res[name] = {"T": w.T, "mean_us": us, "gbs": nbytes / (us * 1e-6) / 1e9, "tflops": flops / (us * 1e-6) / 1e12,
                      "kernel": "router_gemv_kernel" if w.T < 64 else "router_mfma_kernel"}
     res["decode"]["hbm_frac"] = res["decode"]["gbs"] / HBM_PEAK_GBS
-    res["prefill"]["mfma_frac"] = res["prefill"]["tflops"] / BF16_PEAK_TFLOPS
+    res["prefill"]["mfma_frac"] = res["prefill"]["tflops"] / MFMA_F16_PEAK_TFLOPS
     res["workload"] = "router projection, E=512, H=2048, bf16 weights and activations, fp32 logits"
     return res
 
@@ -404,6 +416,8 @@ def bits3_bench(args, torch, moe, synth, oracle):
     """The decode/verify layer and the prefill chunk with 3-bit weights (same routing and shapes)."""
     res, _ = decode_bench(args, torch, moe, synth, oracle, 3)
     pre = None if args.no_prefill else prefill_bench(args, torch, moe, synth, oracle, 3)
+    if pre is not None:
+        pre.pop("_data")
     return {"metric": "MoE-layer tokens/s, 3-bit weights", "unit": "tokens/s",
             "decode": {"workload": "decode/verify layer, T=3, 512 experts, top-10, 2048 x 512, 3-bit",
                        "value": res["value"], "ms_per_step": res["ms_per_step"], "unique_experts_per_step": res["U"],
@@ -413,7 +427,9 @@ def bits3_bench(args, torch, moe, synth, oracle):
 
 def prefill4_bench(args, torch, moe, synth, oracle):
     """The prefill chunk with 4-bit weights (same routing and shapes)."""
-    return {"metric": "MoE-layer prefill tokens/s, 4-bit weights", **prefill_bench(args, torch, moe, synth, oracle, 4)}
+    pre = prefill_bench(args, torch, moe, synth, oracle, 4)
+    pre.pop("_data")
+    return {"metric": "MoE-layer prefill tokens/s, 4-bit weights", **pre}
 
 
 # ---- stacks of layers (decode steps through many layers) ------------------------------------
@@ -756,16 +772,77 @@ def crossover_bench(args, torch, moe, synth, oracle):
     }
 
 
-def cpu_baseline(args, oracle, data):
+def _cpu_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_baseline(args, oracle, data, pre_data=None):
+    """The oracle (scalar C, fp64) on the host cores: the decode layer on one thread and on all threads, and the
+    prefill chunk on all threads (in full) with a one-thread figure built from measured per-expert and per-row
+    costs.  Each timing is the median of ROUNDS rounds."""
+    import numpy as np
     x_np, lg_np, ex, w = data
-    n = args.cpu_steps
-    t0 = time.perf_counter()
-    for _ in range(n):
-        oracle.layer(x_np, lg_np, ex, w.k, w.H, w.I, w.bits, want_y=False)
-    dt = time.perf_counter() - t0
-    return {"value": w.T * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} layer steps of the same workload (T={w.T}), scalar C fp64 oracle on one thread, "
-                      f"{dt:.1f} s"}
+    nt = oracle.default_threads()
+
+    def timed(fn, rounds=ROUNDS):
+        ts = []
+        for _ in range(rounds):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2], min(ts), max(ts)
+
+    n1, nm = max(1, args.cpu_steps // 4), args.cpu_steps
+    med1, lo1, hi1 = timed(lambda: [oracle.layer(x_np, lg_np, ex, w.k, w.H, w.I, w.bits, want_y=False)
+                                    for _ in range(n1)])
+    medm, lom, him = timed(lambda: [oracle.layer(x_np, lg_np, ex, w.k, w.H, w.I, w.bits, want_y=False, nthreads=nt)
+                                    for _ in range(nm)])
+    out = {"value": w.T * nm / medm, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+           "sample": f"decode/verify layer (T={w.T}), {nm} layer steps per round on {nt} threads "
+                     f"(oracle_layer_mt), median of {ROUNDS} rounds ({medm:.2f} s; min {lom:.2f}, max {him:.2f})",
+           "single_thread": {"value": w.T * n1 / med1, "unit": "tokens/s", "cores": 1,
+                             "sample": f"{n1} layer steps per round, median of {ROUNDS} rounds ({med1:.2f} s; "
+                                       f"min {lo1:.2f}, max {hi1:.2f})"},
+           **_cpu_info()}
+    if pre_data is not None:
+        px, plg, pex, pw = pre_data
+        medp, lop, hip = timed(lambda: oracle.layer(px, plg, pex, pw.k, pw.H, pw.I, pw.bits, want_y=False,
+                                                    nthreads=nt), rounds=1)
+        # one thread: the oracle decodes each routed expert once and runs every routed row through the decoded
+        # matrices; time both pieces on this host and scale them to the chunk's counts
+        ids, _ = oracle.route(plg, pw.k)
+        hit = np.unique(ids)
+        t0 = time.perf_counter()
+        mats = [oracle.dequant(pex[hit[0]], pw.H, pw.I, pw.bits, m) for m in range(3)]
+        t_dec = time.perf_counter() - t0
+        xr = (px[:64].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        t0 = time.perf_counter()
+        for r in range(64):
+            oracle.ffn_decoded(*mats, xr[r])
+        t_row = (time.perf_counter() - t0) / 64
+        est = len(hit) * t_dec + ids.size * t_row
+        out["prefill"] = {
+            "value": pw.T / medp, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"the whole 8,192-token chunk (Zipf({1.1 * args.prefill_bias:g}), {len(hit)} experts hit) on "
+                      f"{nt} threads, one round: {medp:.1f} s",
+            "single_thread_estimate": {
+                "value": pw.T / est, "unit": "tokens/s", "cores": 1,
+                "sample": f"extrapolated: {len(hit)} expert decodes x {t_dec * 1e3:.1f} ms (one measured) + "
+                          f"{ids.size} routed rows x {t_row * 1e3:.2f} ms (64 rows measured) = {est:.0f} s"}}
+    return out
 
 
 def main():
@@ -822,9 +899,17 @@ def main():
         return
 
     res, data = decode_bench(args, torch, moe, synth, oracle)
-    pre = None if args.no_prefill else prefill_bench(args, torch, moe, synth, oracle)
+    pre = flat = pre_data = None
+    if not args.no_prefill:
+        pre = prefill_bench(args, torch, moe, synth, oracle)
+        pre_data = pre.pop("_data")
+        flat = prefill_bench(args, torch, moe, synth, oracle, bias=0.21)
+        flat.pop("_data")
+        flat["note"] = ("the Zipf bias scaled by 0.21: every expert is hit and the per-expert row counts span "
+                        f"{flat['min_rows_per_hit_expert']} to {flat['max_rows_per_expert']}")
+        torch.cuda.empty_cache()
     rtr = None if args.no_prefill else router_bench(args, torch, moe, synth, oracle)
-    cpu = None if args.no_cpu else cpu_baseline(args, oracle, data)
+    cpu = None if args.no_cpu else cpu_baseline(args, oracle, data, pre_data)
     out = {
         "metric": METRIC,
         "value": res["value"],
@@ -847,8 +932,10 @@ def main():
             "four_call_us_per_step": res["four_call_us_per_step"],
         },
         "roofline": res["roofline"],
+        "rounds_us_per_step": res["rounds_us_per_step"],
         "cpu_baseline": cpu,
         "prefill": pre,
+        "prefill_flat": flat,
         "router": rtr,
     }
     print(json.dumps(out), flush=True)
