@@ -34,6 +34,10 @@ static int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 #define MOE_STAGE_IN_GATEUP 1
 #endif
 constexpr bool kStageInGateup = MOE_STAGE_IN_GATEUP != 0;
+#ifndef MOE_RESOLVE_IN_GATEUP
+#define MOE_RESOLVE_IN_GATEUP 1
+#endif
+constexpr bool kResolveInGateup = MOE_RESOLVE_IN_GATEUP != 0;
 
 BlobLayout blob_layout(int H, int I, int bits) {
   const int64_t gu_codes = (int64_t)I * H * bits / 8, gu_sm = (int64_t)I * (H / 32) * 4;
@@ -294,6 +298,16 @@ moe_status moe_layer_decode_slots(const moe_qlayer* q, moe_slot_table* t, int la
   if (ws_bytes < W.bytes)
     return fail(MOE_EWORKSPACE, fmt("moe_layer_decode_slots: workspace %lld bytes, needs %lld", (long long)ws_bytes,
                                     (long long)W.bytes));
+  if (kResolveInGateup && gemv_stages_misses(q->H, q->I) && decode_routes_in_gateup(q->H, q->I, T, k)) {
+    FoldedCombine fc;
+    fc.w = w;
+    fc.residual = residual;
+    fc.r_t = r_t;
+    fc.out = out;
+    fc.out_bf16 = out_bf16;
+    return launch_decode_routed_slots(*q, t, layer, logits, x, x_t, T, k, ids, w, offsets, sorted_assign, assign_pos,
+                                      active, n_active, W, y, y_t, fc, stream);
+  }
   if (moe_status st = launch_route_dispatch_resolve(logits, T, q->E, k, ids, w, offsets, sorted_assign, assign_pos,
                                                     active, n_active, W, t, layer, stream))
     return st;

@@ -53,6 +53,7 @@
 // preceding kernel, one dependent load.
 #include "internal.hpp"
 #include "route_dispatch_dev.hpp"
+#include "slot_dev.hpp"
 
 namespace moe {
 namespace {
@@ -255,6 +256,7 @@ struct DecodeArgs {
   void* y;
   const int32_t* rows;   // (expert, assignment) per sorted position
   const int32_t* nrows;  // number of sorted positions
+  const int32_t* pos_slot;  // NULL, or the slot of each sorted position (overrides slot_map in the down rows)
   // combine folded into the row-tiled down kernel (out == nullptr: not folded)
   const float* w;
   const void* residual;
@@ -725,6 +727,21 @@ __device__ __forceinline__ const uint8_t* staged_source(const StageArgs& G, int6
   return nullptr;
 }
 
+// The passes of one gate/up item over its expert's routed rows, reading blob;
+// with STAGE and dst set, the first pass also writes what it reads to dst.
+template <int BITS, int TM, bool SPLIT, int NI, bool STAGE>
+__device__ __forceinline__ void item_gateup_wide_passes(const DecodeArgs& A, const Slot& d, int i0,
+                                                        const uint8_t* blob, uint8_t* dst) {
+  for (int tg = 0; tg < d.ne;) {
+    const int nt = min(d.ne - tg, TM);
+    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
+    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
+    else gateup_pass_wide<BITS, 1, SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
+    tg += nt;
+    dst = nullptr;
+  }
+}
+
 template <int BITS, int TM, bool SPLIT, int NI, bool STAGE = false>
 __device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot& d, int j,
                                                  const StageArgs* G = nullptr) {
@@ -750,14 +767,7 @@ __device__ __forceinline__ void item_gateup_wide(const DecodeArgs& A, const Slot
       blob = src;
     }
   }
-  for (int tg = 0; tg < d.ne;) {
-    const int nt = min(d.ne - tg, TM);
-    if (nt >= 3) gateup_pass_wide<BITS, (TM >= 3 ? 3 : 1), SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
-    else if (nt == 2) gateup_pass_wide<BITS, (TM >= 2 ? 2 : 1), SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
-    else gateup_pass_wide<BITS, 1, SPLIT, NI, STAGE>(A, d, blob, i0, tg, dst);
-    tg += nt;
-    dst = nullptr;
-  }
+  item_gateup_wide_passes<BITS, TM, SPLIT, NI, STAGE>(A, d, i0, blob, dst);
 }
 
 constexpr int kStageUnroll = 4;
@@ -776,6 +786,36 @@ __device__ __forceinline__ void stage_copy(const StageArgs& G, uint8_t* slots, i
     const int64_t ch = w % cpb;
     const uint8_t* src = G.host + (int64_t)G.copies[2 * c + 1] * eb;
     uint8_t* dst = slots + (int64_t)G.copies[2 * c] * eb;
+    uint4 v[kStageUnroll];
+    bool on[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int64_t off = ch * kStageChunk + ((int64_t)u * 256 + threadIdx.x) * 16;
+      bool mine = off < eb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) mine = mine && !(off >= G.item_lo[p] && off < G.item_hi[p]);
+      on[u] = mine;
+      if (mine) v[u] = *reinterpret_cast<const uint4*>(src + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int64_t off = ch * kStageChunk + ((int64_t)u * 256 + threadIdx.x) * 16;
+      if (on[u]) *reinterpret_cast<uint4*>(dst + off) = v[u];
+    }
+  }
+}
+
+// stage_copy with the misses from the record of a resolve published in the
+// same launch (miss_slot, miss_idx: its miss list, read into LDS).
+__device__ __forceinline__ void stage_copy_list(const StageArgs& G, int nc, const int* miss_slot, const int* miss_idx,
+                                                uint8_t* slots, int64_t eb, int cw) {
+  const int64_t cpb = (eb + kStageChunk - 1) / kStageChunk;
+  const int64_t total = (int64_t)nc * cpb;
+  for (int64_t w = cw; w < total; w += G.ncw) {
+    const int c = (int)(w / cpb);
+    const int64_t ch = w % cpb;
+    const uint8_t* src = G.host + (int64_t)miss_idx[c] * eb;
+    uint8_t* dst = slots + (int64_t)miss_slot[c] * eb;
     uint4 v[kStageUnroll];
     bool on[kStageUnroll];
 #pragma unroll
@@ -826,7 +866,7 @@ __device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (
     pr[q] = pp[q];
     const int e = min(max(A.rows[2 * pr[q]], 0), A.E - 1);
     aa[q] = A.rows[2 * pr[q] + 1];
-    const int idx = resident_index(A, e);
+    const int idx = A.pos_slot ? A.pos_slot[pr[q]] : resident_index(A, e);
     res[q] = idx >= 0;
     blob[q] = A.base + (int64_t)(res[q] ? idx : 0) * A.stride;
   }
@@ -904,7 +944,7 @@ __device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (
 }
 
 template <int BITS, bool YBF16>
-__global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
+__device__ __forceinline__ void ffn_down_rows_body(const DecodeArgs& A) {
   __shared__ float ylds[kDecodeMaxRows * kRowTile];
   __shared__ float wl[kDecodeMaxRows];
   const int wave = threadIdx.x >> 6;
@@ -949,6 +989,11 @@ __global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
       A.out_bf16[o] = (uint16_t)(u >> 16);
     }
   }
+}
+
+template <int BITS, bool YBF16>
+__global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
+  ffn_down_rows_body<BITS, YBF16>(A);
 }
 
 // ---- kernels ----------------------------------------------------------------------
@@ -1138,6 +1183,124 @@ moe_status launch_routed_b(DecodeArgs& a, const RouteOut& r, int bits, int max_a
                      : launch_wide_routed<4, SPLIT, YBF16, EPL>(a, r, max_active, s);
 }
 
+// ---- decode step through a slot table, routing and resolve inside gate/up --------------
+// moe_layer_decode_slots for the wide shapes.  Workgroup 0 routes the T
+// tokens, resolves the active experts of `layer` against the table
+// (dev::slot_resolve_publish: stamps and owners written, the outcome recorded,
+// the table's ready word set), then writes the routing and dispatch outputs
+// and the slot of each sorted position for the down launch.  Workgroups
+// 1 .. ncw wait for the record and copy the parts of each missed blob that no
+// gate/up item writes.  The others route the tokens themselves and run one
+// gate/up item each: an expert found in the map runs from its slot at once; a
+// missed one waits for the record, reads its rows from the master copy and
+// writes them into its new slot as it goes.  The map, clock, miss list and
+// counters are written by the down launch that follows (the map is what the
+// items of this launch look experts up in).
+template <int BITS, bool SPLIT, int EPL, int NI>
+__global__ __launch_bounds__(256) void ffn_route_resolve_gateup_kernel(DecodeArgs A, RouteOut R, StageArgs G,
+                                                                       SlotDevArgs SA, int layer, int32_t* pos_slot,
+                                                                       int32_t* record) {
+  __shared__ dev::RouterLds L;
+  __shared__ dev::ResolveLds<256> S;
+  __shared__ int published;
+  const int tid = threadIdx.x, lane = tid & 63;
+  dev::ResolvePrefetch<256> P;
+  if (blockIdx.x == 0) {
+    dev::slot_prefetch_map<256>(SA, layer, P);
+    dev::slot_prefetch_stamps<256>(SA, P);
+    dev::decode_route_lds<EPL, 256>(R.logits, A.T, A.E, A.k, L);
+    const int na = L.na;
+    dev::slot_resolve_publish<256>(SA, layer, L.slot_e, na, record, P, S);
+    dev::decode_route_write<256>(L, A.T, A.E, A.k, R.ids, R.w, R.offsets, R.sorted_assign, R.assign_pos, R.active,
+                                 R.n_active, nullptr, 0, R.rows, R.nrows);
+    for (int s = tid; s < na; s += 256)
+      for (int p = L.slot_p0[s]; p < L.slot_p0[s] + L.slot_ne[s]; ++p) pos_slot[p] = S.slot[s];
+    return;
+  }
+  const int64_t clock = *SA.clock;  // written only between launches
+  const int b = (int)blockIdx.x - 1;
+  if (b < G.ncw) {
+    if (!dev::slot_wait_published(SA, clock, &published)) return;
+    const int nm = dev::rec_word(record, 2);
+    for (int c = tid; c < nm; c += 256) {  // the miss list, in the resolve's LDS (unused here)
+      S.slot[c] = dev::rec_word(record, dev::kRecMissSlot + c);
+      S.rank[c] = dev::rec_word(record, dev::kRecMissIdx + c);
+    }
+    __syncthreads();
+    stage_copy_list(G, nm, S.slot, S.rank, const_cast<uint8_t*>(A.base), A.stride, b);
+    return;
+  }
+  dev::slot_prefetch_map<256>(SA, layer, P);
+  dev::route_ids_lds<EPL, 256>(R.logits, A.T, A.E, A.k, L);
+  dev::slot_map_to_lds<256>(P, S.mapl);
+  __syncthreads();
+  const int i = b - G.ncw, s = i / A.TA, j = i % A.TA;
+  const dev::WaveSlot ws = dev::wave_slot(L, s, A.k);
+  if (ws.e < 0) return;  // the same in every wave: past the active experts
+  const int64_t idx = (int64_t)layer * A.E + ws.e;
+  int slot = __builtin_amdgcn_readfirstlane(S.mapl[ws.e]);
+  const uint8_t* master = nullptr;
+  bool ok = true;
+  if (slot < 0) {  // a miss: its slot comes with the record
+    ok = dev::slot_wait_published(SA, clock, &published);
+    if (ok) slot = __builtin_amdgcn_readfirstlane(dev::rec_word(record, dev::kRecSlot + s));
+    master = G.host + idx * A.stride;
+  }
+  const int wave = tid >> 6, i0 = (j * 4 + wave) * NI;
+  if (i0 >= A.I) return;
+  if (!ok) {  // no record in time: mark this item's h rows invalid (bf16 quiet NaN)
+    if (lane < NI && i0 + lane < A.I)
+      for (int t = 0; t < ws.ne; ++t) {
+        const size_t o = (size_t)(ws.p0 + t) * A.I + i0 + lane;
+        A.hh[o] = 0x7FC0;
+        A.hl[o] = 0;
+      }
+    return;
+  }
+  uint8_t* slot_blob = const_cast<uint8_t*>(A.base) + (int64_t)slot * A.stride;
+  const Slot d{nullptr, ws.e, ws.p0, ws.ne, ws.tokv};
+  if (!master) {
+    item_gateup_wide_passes<BITS, kWideTM, SPLIT, NI, false>(A, d, i0, slot_blob, nullptr);
+  } else {  // a miss: every pass reads the master copy, the first one also fills the slot (NI/2 rows at a time)
+    constexpr int NH = NI > 2 ? NI / 2 : NI;
+    for (int i1 = i0; i1 < i0 + NI && i1 < A.I; i1 += NH)
+      item_gateup_wide_passes<BITS, kWideTM, SPLIT, NH, true>(A, d, i1, master, slot_blob);
+  }
+}
+
+// Down rows of a decode step through a slot table: the slot of each sorted
+// position comes from the gate/up launch (A.pos_slot); workgroup 0 also writes
+// the resolve's outcome into the table state (nothing reads the old state any
+// more).
+template <int BITS, bool YBF16>
+__global__ __launch_bounds__(1024) void ffn_down_rows_commit_kernel(DecodeArgs A, SlotDevArgs SA,
+                                                                    const int32_t* record) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) dev::slot_record_commit(SA, record);
+  ffn_down_rows_body<BITS, YBF16>(A);
+}
+
+template <int BITS, bool SPLIT, bool YBF16, int EPL, int NI = kRoutedNI<BITS, SPLIT>>
+moe_status launch_resolve_routed(DecodeArgs& a, const RouteOut& r, const StageArgs& g, const SlotDevArgs& sa,
+                                 int layer, int32_t* pos_slot, int32_t* record, int max_active, hipStream_t s) {
+  a.TA = (int)ceil_div(a.I, 4 * NI);
+  launch_k(MOE_KERNEL_GEMV_GATEUP, ffn_route_resolve_gateup_kernel<BITS, SPLIT, EPL, NI>,
+           dim3((unsigned)(1 + g.ncw + max_active * a.TA)), dim3(256), 0, s, a, r, g, sa, layer, pos_slot, record);
+  if (moe_status st = check_launch("ffn_route_resolve_gateup")) return st;
+  a.pos_slot = pos_slot;
+  launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_commit_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
+           dim3(64 * kRowWaves), 0, s, a, sa, (const int32_t*)record);
+  return check_launch("ffn_down");
+}
+
+template <bool SPLIT, bool YBF16, int EPL>
+moe_status launch_resolve_routed_b(DecodeArgs& a, const RouteOut& r, const StageArgs& g, const SlotDevArgs& sa,
+                                   int layer, int32_t* pos_slot, int32_t* record, int bits, int max_active,
+                                   hipStream_t s) {
+  return bits == 2   ? launch_resolve_routed<2, SPLIT, YBF16, EPL>(a, r, g, sa, layer, pos_slot, record, max_active, s)
+         : bits == 3 ? launch_resolve_routed<3, SPLIT, YBF16, EPL>(a, r, g, sa, layer, pos_slot, record, max_active, s)
+                     : launch_resolve_routed<4, SPLIT, YBF16, EPL>(a, r, g, sa, layer, pos_slot, record, max_active, s);
+}
+
 template <int BITS, int TM, bool SPLIT, bool YBF16>
 moe_status launch_tm(DecodeArgs& a, int max_active, hipStream_t s) {
   constexpr int RLA = SPLIT ? kRLGateUpSplit<TM> : kRLGateUp<TM>;
@@ -1220,6 +1383,10 @@ DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I) {
   off += up((size_t)n * 2 * 4);
   W.nrows = reinterpret_cast<int32_t*>(b + off);
   off += 256;
+  W.pos_slot = reinterpret_cast<int32_t*>(b + off);
+  off += up((size_t)n * 4);
+  W.record = reinterpret_cast<int32_t*>(b + off);
+  off += up((size_t)dev::kSlotRecordWords * 4);
   W.bytes = off;
   return W;
 }
@@ -1311,6 +1478,59 @@ moe_status launch_decode_routed(const moe_qlayer& q, const float* logits, const 
                      : launch_routed_b<false, true, 8>(a, r, q.bits, max_active, s);
   return big ? launch_routed_b<false, false, 16>(a, r, q.bits, max_active, s)
              : launch_routed_b<false, false, 8>(a, r, q.bits, max_active, s);
+}
+
+moe_status launch_decode_routed_slots(const moe_qlayer& q, const moe_slot_table* t, int layer, const float* logits,
+                                      const void* x, moe_dtype x_t, int T, int k, int32_t* ids, float* w,
+                                      int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, int32_t* active,
+                                      int32_t* n_active, const DecodeWs& W, void* y, moe_dtype y_t,
+                                      const FoldedCombine& fc, hipStream_t s) {
+  if (!decode_routes_in_gateup(q.H, q.I, T, k) || !fc.out)
+    return fail(MOE_EUNSUPPORTED, "routing and resolve cannot be fused into the gate/up launch for this shape");
+  DecodeArgs a = make_args(q, x, T, k, sorted_assign, n_active, W, y);
+  a.w = w;
+  a.residual = fc.residual;
+  a.r_bf16 = fc.r_t == MOE_BF16;
+  a.out = fc.out;
+  a.out_bf16 = fc.out_bf16;
+  RouteOut r;
+  r.logits = logits;
+  r.ids = ids;
+  r.w = w;
+  r.offsets = offsets;
+  r.sorted_assign = sorted_assign;
+  r.assign_pos = assign_pos;
+  r.active = active;
+  r.n_active = n_active;
+  r.rows = W.rows;
+  r.nrows = W.nrows;
+  const SlotTableView v = slot_table_view(t);
+  const BlobLayout L = blob_layout(q.H, q.I, q.bits);
+  const int64_t codes = (int64_t)q.I * q.H * q.bits / 8, sm = (int64_t)q.I * (q.H / 32) * 4;
+  StageArgs g{};
+  g.host = v.host_dev;
+  g.item_lo[0] = L.gate_codes;
+  g.item_hi[0] = L.gate_codes + codes;
+  g.item_lo[1] = L.gate_sm;
+  g.item_hi[1] = L.gate_sm + sm;
+  g.item_lo[2] = L.up_codes;
+  g.item_hi[2] = L.up_codes + codes;
+  g.item_lo[3] = L.up_sm;
+  g.item_hi[3] = L.up_sm + sm;
+  g.ncw = kStageCopyGroups;
+  const SlotDevArgs sa = slot_dev_args(t);
+  const int max_active = (int)std::min<int64_t>(q.E, (int64_t)T * k);
+  const bool split = x_t == MOE_F32, yb = y_t == MOE_BF16, big = q.E > 512;
+  if (split) {
+    if (yb) return big ? launch_resolve_routed_b<true, true, 16>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s)
+                       : launch_resolve_routed_b<true, true, 8>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s);
+    return big ? launch_resolve_routed_b<true, false, 16>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s)
+               : launch_resolve_routed_b<true, false, 8>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s);
+  }
+  if (yb) return big ? launch_resolve_routed_b<false, true, 16>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s)
+                     : launch_resolve_routed_b<false, true, 8>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s);
+  return big ? launch_resolve_routed_b<false, false, 16>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s)
+             : launch_resolve_routed_b<false, false, 8>(a, r, g, sa, layer, W.pos_slot, W.record, q.bits, max_active, s);
 }
 
 moe_status launch_ffn_gemv(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k, const int32_t* offsets,

@@ -60,6 +60,8 @@ struct DecodeWs {
   SlotDesc* desc;
   int32_t* rows;   // [T*k][2]
   int32_t* nrows;  // [1]
+  int32_t* pos_slot;  // [T*k] slot of each sorted position (decode through a slot table)
+  int32_t* record;    // a slot-table resolve outcome (decode through a slot table)
   size_t bytes;
 };
 DecodeWs decode_ws(void* ws, int T, int k, int E, int H, int I);
@@ -125,6 +127,17 @@ struct MissStage {
   const uint8_t* host = nullptr;     // device view of the page-locked master copy
 };
 bool gemv_stages_misses(int H, int I);
+
+// moe_layer_decode_slots for the shapes decode_routes_in_gateup accepts, in two
+// launches: gate/up with the routing, the table's resolve (evaluated by every
+// workgroup from the state before the launch; the last workgroup to finish
+// writes the new state) and the staging of the misses; then down with the
+// combine folded in.
+moe_status launch_decode_routed_slots(const moe_qlayer& q, const moe_slot_table* t, int layer, const float* logits,
+                                      const void* x, moe_dtype x_t, int T, int k, int32_t* ids, float* w,
+                                      int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, int32_t* active,
+                                      int32_t* n_active, const DecodeWs& W, void* y, moe_dtype y_t,
+                                      const FoldedCombine& fc, hipStream_t s);
 
 moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x_t, int T, int k,
                                  const int32_t* sorted_assign, const int32_t* n_active, const DecodeWs& W, void* y,

@@ -69,6 +69,7 @@ struct moe_slot_table {
   uint64_t* d_stats = nullptr;        // [5] hits, misses, bytes_h2d, resolves, evictions
   int32_t* d_copies = nullptr;        // [2 * E] (slot, l*E + e) of the last resolve's misses
   int32_t* d_ncopies = nullptr;       // [1]
+  uint64_t* d_ready = nullptr;        // [1] see SlotDevArgs::ready
 };
 
 namespace {
@@ -171,7 +172,7 @@ moe_status resolve_list(moe_slot_table* t, int layer, const int32_t* act, int n,
 
 // ---- device mode -------------------------------------------------------------------------
 struct DevLayout {
-  size_t owner, stamp, clock, stats, copies, ncopies, bytes;
+  size_t owner, stamp, clock, stats, copies, ncopies, ready, bytes;
 };
 
 DevLayout dev_layout(int E, int n_slots) {
@@ -189,6 +190,8 @@ DevLayout dev_layout(int E, int n_slots) {
   d.copies = off;
   off += up((size_t)E * 8);
   d.ncopies = off;
+  off += 256;
+  d.ready = off;
   off += 256;
   d.bytes = off;
   return d;
@@ -425,6 +428,7 @@ moe_status moe_slot_table_enable_device(moe_slot_table* t, void* state, size_t s
   t->d_stats = reinterpret_cast<uint64_t*>(b + d.stats);
   t->d_copies = reinterpret_cast<int32_t*>(b + d.copies);
   t->d_ncopies = reinterpret_cast<int32_t*>(b + d.ncopies);
+  t->d_ready = reinterpret_cast<uint64_t*>(b + d.ready);
   const int32_t zero = 0;
   const char* what = "moe_slot_table_enable_device: upload";
   if (moe_status st = moe::check_hip(hipMemcpy(t->d_owner, t->owner.data(), sizeof(int32_t) * t->n_slots,
@@ -438,6 +442,10 @@ moe_status moe_slot_table_enable_device(moe_slot_table* t, void* state, size_t s
   if (moe_status st = moe::check_hip(hipMemcpy(t->d_stats, stats, sizeof(stats), hipMemcpyHostToDevice), what))
     return st;
   if (moe_status st = moe::check_hip(hipMemcpy(t->d_ncopies, &zero, sizeof(zero), hipMemcpyHostToDevice), what))
+    return st;
+  // the ready word of the in-launch resolve: never clock + 1 for a clock yet to come
+  const uint64_t ready = (uint64_t)clock;
+  if (moe_status st = moe::check_hip(hipMemcpy(t->d_ready, &ready, sizeof(ready), hipMemcpyHostToDevice), what))
     return st;
   t->host_dev = static_cast<const uint8_t*>(hd);
   t->device_mode = true;
@@ -476,6 +484,7 @@ SlotDevArgs slot_dev_args(const moe_slot_table* t) {
   a.stats = t->d_stats;
   a.copies = t->d_copies;
   a.ncopies = t->d_ncopies;
+  a.ready = t->d_ready;
   a.E = t->E;
   a.n_slots = t->n_slots;
   a.expert_bytes = t->expert_bytes;

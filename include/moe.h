@@ -332,13 +332,18 @@ size_t moe_slot_table_device_bytes(int L, int E, int n_slots);
  * (moe_slot_table_resolve_device's policy), then the gate/up and down kernels
  * run on the slots.  Strata feature (tech.hub77a.com), section
  * "2. 왜 대단한가" (2): resident experts are used at once while the missing
- * ones move in from host RAM.  When H % 2048 == 0 and I % 512 == 0 the misses
- * are staged inside the gate/up launch (three launches): the gate/up rows of
- * a missed expert are read from the master copy and written into its slot as
- * they are used, while the resident experts' rows run beside them and
- * workgroups of the same grid copy the rest of each missed blob.  Other
- * shapes copy the misses in a launch of their own first (four launches, or
- * five when the combine cannot be folded).  q must be the table's view of `layer`:
+ * ones move in from host RAM.  When H % 2048 == 0 and I % 512 == 0 the step
+ * is two launches: in the gate/up launch one workgroup
+ * routes and resolves and publishes the outcome through the table's device
+ * state, the workgroups of resident experts run at once, and those of missed
+ * experts wait for it, then read their gate/up rows from the master copy and
+ * write them into the new slot as they are used, while other workgroups of
+ * the grid copy the rest of each missed blob; the down launch (combine
+ * folded) also writes the table's map, miss list and counters.  Other shapes
+ * route and resolve in a launch of their own, then copy the misses in a
+ * launch of their own or inside gate/up (four launches, or five when the
+ * combine cannot be folded).  Two calls on one table must not overlap (one
+ * stream).  q must be the table's view of `layer`:
  * base = slots, stride = expert_bytes, slot_map = map + layer * E.  Outputs
  * and workspace as moe_layer_decode (moe_layer_decode_workspace_bytes); every
  * output is bit-identical to moe_layer_decode on resident weights.
