@@ -33,6 +33,11 @@
 // weights alone already moves outputs by 4e-3 to 9e-3 of their row maximum.
 // Both types run at the same MFMA rate on gfx950.
 //
+// Two kernels.  mfma_rb_kernel (below, used when H % 256 == 0 and I % 128 ==
+// 0) decodes each wave's weight rows straight into MFMA operand registers and
+// stages only the activations in LDS; mfma_ffn_kernel, described next, decodes
+// the weight tile into LDS and serves every other shape.
+//
 // Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile
 // (128 x 256); each wave owns 64 x 128, i.e. 4 x 8 fragments of 16 x 16, so
 // every fragment read from LDS feeds 4 to 8 MFMAs.  A wave's four 16-row
@@ -59,6 +64,8 @@
 // A small prep kernel turns (n_active, active, offsets) into the list of
 // (expert slot, first row) M-tiles; the GEMM grid is sized for the worst case
 // and blocks past the list's end exit at once.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace moe {
@@ -103,6 +110,16 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 
 // Saturate finite values to the fp16 range; NaN stays NaN.
 __device__ __forceinline__ float sat_f16(float v) { return fabsf(v) > kF16Max ? copysignf(kF16Max, v) : v; }
+
+// h' = g' * sigmoid(g' * 2^e) * u' with the hardware exp2 and reciprocal (each
+// within about 1 ulp in fp32; h' is then rounded to fp16): exp(-z) overflows
+// to +inf for large negative z, giving h' = -0, and underflows to 0 for large
+// positive z, giving g' * u'; NaN stays NaN.
+__device__ __forceinline__ float swiglu_scaled(float g, float u, int ex) {
+  const float z = __builtin_amdgcn_ldexpf(g, ex);
+  const float en = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + en) * u;
+}
 
 __device__ __forceinline__ float f16lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
@@ -706,8 +723,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
         const int i = nt * (kBN / 2) + 8 * (FN * wn + fj) + fcol / 2;
         if (i >= A.I) continue;
         const f32x4_t v = acc[fi][fj];
-        float h0 = v[0] / (1.0f + expf(-__builtin_amdgcn_ldexpf(v[0], ex))) * v[2];
-        float h1 = v[1] / (1.0f + expf(-__builtin_amdgcn_ldexpf(v[1], ex))) * v[3];
+        const float h0 = swiglu_scaled(v[0], v[2], ex);
+        const float h1 = swiglu_scaled(v[1], v[3], ex);
         sat += (fabsf(h0) > kF16Max) + (fabsf(h1) > kF16Max);
         *reinterpret_cast<uint32_t*>(hrow + i) = pack_f16(sat_f16(h0), sat_f16(h1));
       }
@@ -736,6 +753,385 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
   }
 }
 
+// ---- weights decoded into registers (32 x 32 x 16 MFMA) ------------------------
+// The same GEMMs with the B tile never in LDS.  Each of the 4 waves owns 64
+// of the tile's 256 weight rows for all 128 tile rows: 4 x 2 fragments of
+// v_mfma_f32_32x32x16_f16 (weights as the first operand: D[n][t]).  A lane
+// supplies 8 K-values of one weight row per MFMA, so it decodes those
+// weights itself, straight into the operand registers, from the row's codes
+// and scale/min loaded into registers two K-steps at a time; no two waves
+// decode the same row.  Only the activation tile goes through LDS (8 KB per
+// K-step).  Weight rows are placed so that a lane's 16 outputs of a fragment
+// are 8 consecutive h columns (gate/up: gate and up of each i in the same
+// lane) or 16 consecutive y columns (down): one 16-byte store per 8 values.
+//
+// Operand layouts (32 x 32 x 16, f16): lane l gives row l % 32 of the first
+// operand and column l % 32 of the second, K-values 8 (l / 32) .. + 8 of the
+// 16; it receives D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32] in accumulator v.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Activation tile rows (64 bytes) with chunk c stored at c ^ ((row >> 2) & 3):
+// the fragment reads (32 consecutive rows, one chunk per half-wave) then touch
+// each bank once per 16 lanes.
+__device__ __forceinline__ int lds_off_rb(int row, int chunk) { return row * kPitch + ((chunk ^ ((row >> 2) & 3)) * 8); }
+
+// The 2-bit table of one (row, block): entries fp16_rne(fp32 fma(s, q, m)), q = 0..3.
+struct Lut2 {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ Lut2 lut2(uint32_t smw) {
+  const float s = f16lo(smw), m = f16hi(smw);
+  return Lut2{pack_f16(__builtin_fmaf(s, 0.f, m), __builtin_fmaf(s, 1.f, m)),
+              pack_f16(__builtin_fmaf(s, 2.f, m), __builtin_fmaf(s, 3.f, m))};
+}
+
+// 8 weights (4 packed pairs) of one row for K-half kh of a K-step, lane half
+// hh = l / 32 (weights 16 kh + 8 hh .. + 8 of the block).  c: the K-step's code
+// words (2-bit: one per 16 weights; 3-bit: low bits of each half, then the
+// high-bit word; 4-bit: two per 16 weights).
+template <int BITS>
+__device__ __forceinline__ void dec8(const uint32_t* c, int kh, int hh, const Lut2& t, const Dec16& d,
+                                     uint32_t (&o)[4]) {
+  if constexpr (BITS == 2) {
+    const uint32_t w = c[kh] >> (8 * hh);  // pairs 4 hh .. 4 hh + 3 at bits 2j / 16 + 2j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t q2 = (w >> (2 * j)) & 0x00030003u;
+      o[j] = __builtin_amdgcn_perm(t.hi, t.lo, q2 * 0x0202u + 0x01000100u);
+    }
+  } else if constexpr (BITS == 3) {
+    const uint32_t lo = c[kh] >> (8 * hh), hi = (c[2] >> (8 * kh)) >> (4 * hh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t h2 = ((hi >> j) & 0x00010001u) << 2;
+      o[j] = dec_pair(and_or(lo >> (2 * j), 0x00030003u, 0x64006400u | h2), d);
+    }
+  } else {
+    const uint32_t w = hh ? c[2 * kh + 1] : c[2 * kh];  // pairs at bits 4j / 16 + 4j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = dec_pair(and_or(w >> (4 * j), 0x000F000Fu, 0x64006400u), d);
+  }
+}
+
+template <int BITS, bool GATEUP, bool YBF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_rb_kernel(GemmArgs A) {
+  constexpr int BM = 128, BN = 256, NT = 256, A_CHUNKS = 2;
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][BM * kPitch];
+
+  const int xcd = blockIdx.x % kXcd, jb = blockIdx.x / kXcd;
+  int tile_idx, nt;
+  if (MOE_MFMA_XCD_RANGE == 2 || (MOE_MFMA_XCD_RANGE == 1 && GATEUP)) {
+    const int count = *A.tile_count, per_die = (count + kXcd - 1) / kXcd, jt = jb / A.n_tiles_n;
+    tile_idx = xcd * per_die + jt;
+    nt = jb % A.n_tiles_n;
+    if (jt >= per_die || tile_idx >= count) return;
+  } else {
+    tile_idx = (jb / A.n_tiles_n) * kXcd + xcd;
+    nt = jb % A.n_tiles_n;
+    if (tile_idx >= *A.tile_count) return;
+  }
+  const TileInfo ti = A.tiles[tile_idx];
+  const int e = A.active[ti.slot];
+  const int p_begin = A.offsets[e] + ti.m0;
+  const int rows = min(BM, A.offsets[e + 1] - p_begin);
+  const int idx = A.slot_map ? A.slot_map[e] : e;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, jl = lane & 31;
+  const int nv = (rows + 31) / 32;  // 32-row fragments holding rows of the tile
+  const int K = GATEUP ? A.H : A.I;
+  const int KS = K / kBK;
+
+  if (idx < 0) {  // expert not resident: NaN outputs, no weight reads
+    const float nan = __builtin_nanf("");
+    constexpr int COLS = GATEUP ? BN / 2 : BN;
+    for (int c = tid; c < BM * COLS; c += NT) {
+      const int m = c / COLS, col = c % COLS;
+      if (m >= rows) continue;
+      if constexpr (GATEUP) {
+        reinterpret_cast<_Float16*>(A.out)[(size_t)(p_begin + m) * A.I + nt * COLS + col] = (_Float16)nan;
+      } else {
+        const int64_t a = A.sorted_assign[p_begin + m];
+        if constexpr (YBF16) reinterpret_cast<__bf16*>(A.out)[a * A.H + nt * COLS + col] = (__bf16)nan;
+        else reinterpret_cast<float*>(A.out)[a * A.H + nt * COLS + col] = nan;
+      }
+    }
+    return;
+  }
+  const uint8_t* blob = A.base + (int64_t)idx * A.stride;
+
+  // ---- activation tile: two 16-byte chunks per thread per K-step ----------------
+  int a_voff[A_CHUNKS], a_lds[A_CHUNKS];
+#pragma unroll
+  for (int jj = 0; jj < A_CHUNKS; ++jj) {
+    const int c = tid + NT * jj, m = c / 4, ch = c % 4;
+    int64_t row;  // rows past the tile's end read the all-zero row kept after the last source row
+    if constexpr (GATEUP) row = m < rows ? A.sorted_assign[p_begin + m] / A.k : A.a_zero_row;
+    else row = m < rows ? p_begin + m : A.a_zero_row;
+    a_voff[jj] = (int)(row * (int64_t)K * 2) + ch * 16;
+    a_lds[jj] = lds_off_rb(m, ch);
+  }
+
+  // ---- this lane's weight rows (one per 32-row fragment fn) ----------------------
+  // fragment row j = lane % 32 = 8 g + 4 hb + r (g < 4, hb, r < 4):
+  //   gate/up: plane r >> 1 (gate, up), i = nt*128 + 32*wave + 16*fn + 8*hb + 2*g + (r & 1)
+  //   down:    n = nt*256 + 64*wave + 32*fn + 16*hb + 4*g + r
+  const int64_t row_code_bytes = (int64_t)K * BITS / 8, row_sm_bytes = (int64_t)(K / 32) * 4;
+  int bc_voff[2], bs_voff[2];
+  {
+    const int g = jl >> 3, hb = (jl >> 2) & 1, r = jl & 3;
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      int64_t row, oc, os;
+      if constexpr (GATEUP) {
+        const int i = nt * (BN / 2) + 32 * wave + 16 * fn + 8 * hb + 2 * g + (r & 1);
+        row = i < A.I ? i : 0;
+        oc = (r >> 1) ? A.off_c1 : A.off_c0;
+        os = (r >> 1) ? A.off_s1 : A.off_s0;
+      } else {
+        const int n = nt * BN + 64 * wave + 32 * fn + 16 * hb + 4 * g + r;
+        row = n < A.H ? n : 0;
+        oc = A.off_c0;
+        os = A.off_s0;
+      }
+      bc_voff[fn] = (int)(oc + row * row_code_bytes);
+      bs_voff[fn] = (int)(os + row * row_sm_bytes);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(A.a_src), (short)0, kBufRecords, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, kBufRecords, kBufFlags);
+
+  struct BPair {  // two K-steps of both rows: codes (BITS words per K-step) and scale/min words
+    uint32_t w[2][2 * BITS];
+    uint2 sm[2];
+  };
+  auto load_a = [&](uint4 (&a)[A_CHUNKS], int ks) {
+#pragma unroll
+    for (int jj = 0; jj < A_CHUNKS; ++jj)
+      a[jj] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, a_voff[jj], ks * kBK * 2, 0));
+  };
+  auto store_a = [&](const uint4 (&a)[A_CHUNKS], int buf) {
+#pragma unroll
+    for (int jj = 0; jj < A_CHUNKS; ++jj) *reinterpret_cast<uint4*>(&lds_a[buf][a_lds[jj]]) = a[jj];
+  };
+  auto load_bpair = [&](BPair& bp, int ks) {  // ks even, ks + 1 < KS
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      if constexpr (BITS == 3) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const uint2 v = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bc_voff[fn] + 8 * j, ks * (4 * BITS), 0));
+          bp.w[fn][2 * j] = v.x;
+          bp.w[fn][2 * j + 1] = v.y;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < BITS / 2; ++j) {
+          const uint4 v = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bc_voff[fn] + 16 * j, ks * (4 * BITS), 0));
+          bp.w[fn][4 * j] = v.x;
+          bp.w[fn][4 * j + 1] = v.y;
+          bp.w[fn][4 * j + 2] = v.z;
+          bp.w[fn][4 * j + 3] = v.w;
+        }
+      }
+      bp.sm[fn] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bs_voff[fn], ks * 4, 0));
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+
+  // ---- the K-step pieces -------------------------------------------------------
+  // Tables of K-step e of pair bp for this lane's two rows.
+  auto tables = [&](const BPair& bp, int e, Lut2 (&t)[2], Dec16 (&d)[2]) {
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      const uint32_t smw = e ? bp.sm[fn].y : bp.sm[fn].x;
+      if constexpr (BITS == 2) t[fn] = lut2(smw);
+      else d[fn] = dec16(smw);
+    }
+  };
+  // Weight operands of K-half kh of K-step e of pair bp.
+  auto dec_half = [&](const BPair& bp, int e, int kh, const Lut2 (&t)[2], const Dec16 (&d)[2], f16x8_t (&bo)[2]) {
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      uint32_t o[4];
+      dec8<BITS>(bp.w[fn] + e * BITS, kh, hh, t[fn], d[fn], o);
+      bo[fn] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  };
+  // Activation operands of K-half kh from LDS buffer `cur`.
+  auto read_a = [&](int cur, int kh, f16x8_t (&ao)[4]) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+      ao[fm] = *reinterpret_cast<const f16x8_t*>(&lds_a[cur][lds_off_rb(32 * fm + jl, 2 * kh + hh)]);
+  };
+  // The MFMAs of one K-half over the first NV fragment rows (NV = 0: the
+  // first nv, a runtime count), with `work` (the next operands' loads from LDS
+  // and decode) issued between them when NV is fixed.
+  auto mfma_half = [&](auto nvc, const f16x8_t (&bo)[2], const f16x8_t (&ao)[4], auto&& work) {
+    constexpr int NV = decltype(nvc)::value;
+    if constexpr (NV == 0) {
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+        if (fm >= nv) break;
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bo[fn], ao[fm], acc[fm][fn], 0, 0, 0);
+      }
+      work();
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < NV; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bo[fn], ao[fm], acc[fm][fn], 0, 0, 0);
+      work();
+#pragma unroll
+      for (int i = 0; i < 2 * NV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five VALU
+      }
+    }
+  };
+
+  // Pipeline: activation chunks two K-steps ahead in registers (sa0 even
+  // stages, sa1 odd), LDS double-buffered with one barrier per K-step; weight
+  // pairs bp0 (stages 4j, 4j+1) and bp1 (4j+2, 4j+3) loaded two K-steps
+  // before their first use.  A K-half's operands (activation fragments from
+  // LDS, weights decoded from the pair registers) are prepared under the
+  // MFMAs of the K-half before.  For 2-bit codes the loop is specialised on
+  // the number of filled fragment rows (nv), so that it has no branch but the
+  // loop's own and the scheduler can interleave the decode with the MFMAs.
+  // Loads past the end repeat the last K-step or pair and are never used.
+  auto run = [&](auto nvc) {
+    constexpr int NV = decltype(nvc)::value;
+    uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
+    BPair bp0, bp1;
+    load_a(sa0, 0);
+    load_a(sa1, min(1, KS - 1));
+    load_bpair(bp0, 0);
+    load_bpair(bp1, 2);
+    store_a(sa0, 0);
+    __syncthreads();
+    load_a(sa0, min(2, KS - 1));
+    f16x8_t ao0[4], ao1[4], bo[2], bo2[2];
+    Lut2 t[2] = {};
+    Dec16 d[2] = {};
+    read_a(0, 0, ao0);
+    tables(bp0, 0, t, d);
+    dec_half(bp0, 0, 0, t, d, bo);
+    __builtin_amdgcn_sched_barrier(0);
+    // One K-step (LDS buffer `buf`) on pair `cur` (its K-step ec); `nxt`, en:
+    // the next K-step's pair; a_next: the next K-step's activation chunks.
+    auto step = [&](int buf, const BPair& cur, int ec, const BPair& nxt, int en, const uint4 (&a_next)[A_CHUNKS]) {
+      mfma_half(nvc, bo, ao0, [&] {
+        read_a(buf, 1, ao1);
+        dec_half(cur, ec, 1, t, d, bo2);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(nvc, bo2, ao1, [&] {
+        tables(nxt, en, t, d);
+        dec_half(nxt, en, 0, t, d, bo);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(a_next, buf ^ 1);
+      __syncthreads();
+      read_a(buf ^ 1, 0, ao0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kb = 0; kb < KS; kb += 4) {
+      step(0, bp0, 0, bp0, 1, sa1);  // stage kb (sa1: stage kb + 1)
+      load_a(sa1, min(kb + 3, KS - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      step(1, bp0, 1, bp1, 0, sa0);  // stage kb + 1 (sa0: stage kb + 2)
+      load_a(sa0, min(kb + 4, KS - 1));
+      load_bpair(bp0, min(kb + 4, KS - 2));
+      __builtin_amdgcn_sched_barrier(0);
+      step(0, bp1, 0, bp1, 1, sa1);  // stage kb + 2
+      load_a(sa1, min(kb + 5, KS - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      step(1, bp1, 1, bp0, 0, sa0);  // stage kb + 3
+      load_a(sa0, min(kb + 6, KS - 1));
+      load_bpair(bp1, min(kb + 6, KS - 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if constexpr (BITS == 2) {  // the specialised loops fit the register budget for 2-bit codes only
+    switch (nv) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
+    }
+  } else {
+    run(std::integral_constant<int, 0>{});
+  }
+
+  // ---- epilogue: lane holds token row 32 fm + lane % 32 of the tile ----------------
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+    const int m = 32 * fm + jl;
+    if (fm >= nv || m >= rows) continue;
+    if constexpr (GATEUP) {
+      // accumulator 4 g + s: gate of i = base + 2 g + s; 4 g + 2 + s: its up (s = 0, 1); all
+      // 2^-e_t times their true values: h' = g' * sigmoid(g' * 2^e_t) * u' = h * 2^(-2 e_t)
+      _Float16* hrow = reinterpret_cast<_Float16*>(A.out) + (size_t)(p_begin + m) * A.I;
+      const int ex = A.xexp[A.sorted_assign[p_begin + m] / A.k];
+      int sat = 0;
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) {
+        const int i0 = nt * (BN / 2) + 32 * wave + 16 * fn + 8 * hh;
+        const f32x16_t v = acc[fm][fn];
+        uint32_t pk[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float g0 = v[4 * g], g1 = v[4 * g + 1], u0 = v[4 * g + 2], u1 = v[4 * g + 3];
+          const float h0 = swiglu_scaled(g0, u0, ex);
+          const float h1 = swiglu_scaled(g1, u1, ex);
+          sat += (fabsf(h0) > kF16Max) + (fabsf(h1) > kF16Max);
+          pk[g] = pack_f16(sat_f16(h0), sat_f16(h1));
+        }
+        *reinterpret_cast<uint4*>(hrow + i0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+      if (sat) atomicAdd(A.clip, (uint32_t)sat);
+    } else {
+      const int64_t a = A.sorted_assign[p_begin + m];
+      const int ey = 2 * A.xexp[a / A.k];
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) {
+        const int n0 = nt * BN + 64 * wave + 32 * fn + 16 * hh;
+        f32x16_t v = acc[fm][fn];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = __builtin_amdgcn_ldexpf(v[r], ey);
+        if constexpr (YBF16) {
+          uint32_t pk[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            pk[q] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q + 1]) << 16);
+          uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(A.out) + a * A.H + n0);
+          dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        } else {
+          float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(A.out) + a * A.H + n0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+      }
+    }
+  }
+}
+
 // 128 x 256 tiles with 256 threads (two workgroups per CU).  256 x 256 tiles
 // with 512 threads share one decoded B tile between twice the rows (a third
 // fewer M-tiles on the prefill workload) but measured no faster.
@@ -748,6 +1144,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
 #ifndef MOE_MFMA_BN_DN
 #define MOE_MFMA_BN_DN 256
 #endif
+#ifndef MOE_MFMA_REGB
+#define MOE_MFMA_REGB 1
+#endif
+constexpr bool kRegB = MOE_MFMA_REGB != 0;
 constexpr int kBM = MOE_MFMA_BM;
 constexpr int kBNGateUp = MOE_MFMA_BN_GU;
 constexpr int kBNDown = MOE_MFMA_BN_DN;
@@ -835,7 +1235,12 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   constexpr int64_t kOff = int64_t(1) << 31;
   constexpr bool kPairOk = true;
   const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
-  if (kPairOk && off_ok && q.H % 128 == 0)
+  // Weights decoded into registers: whole 128-column h tiles and 256-column y tiles.
+  const bool rb = kRegB && off_ok && q.H % 256 == 0 && q.I % 128 == 0;
+  if (rb)
+    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_rb_kernel<BITS, true, false>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
+             dim3(256), 0, s, a);
+  else if (kPairOk && off_ok && q.H % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk, kNT>,
              dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
@@ -850,7 +1255,10 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   a.a_zero_row = n;
   a.n_tiles_n = (int)ceil_div(q.H, kBNDown);
   a.out = y;
-  if (kPairOk && off_ok && q.I % 128 == 0)
+  if (rb)
+    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_rb_kernel<BITS, false, YBF16>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
+             dim3(256), 0, s, a);
+  else if (kPairOk && off_ok && q.I % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, kPairOk, kNT>,
              dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
