@@ -33,10 +33,11 @@
 // weights alone already moves outputs by 4e-3 to 9e-3 of their row maximum.
 // Both types run at the same MFMA rate on gfx950.
 //
-// Two kernels.  mfma_rb_kernel (below, used when H % 256 == 0 and I % 128 ==
-// 0) decodes each wave's weight rows straight into MFMA operand registers and
-// stages only the activations in LDS; mfma_ffn_kernel, described next, decodes
-// the weight tile into LDS and serves every other shape.
+// Two kernels.  mfma_rb_kernel (below, used for 2- and 4-bit codes when
+// H % 256 == 0 and I % 128 == 0) decodes each wave's weight rows straight into
+// MFMA operand registers and stages only the activations in LDS;
+// mfma_ffn_kernel, described next, decodes the weight tile into LDS and serves
+// 3-bit codes and every other shape.
 //
 // Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile
 // (128 x 256); each wave owns 64 x 128, i.e. 4 x 8 fragments of 16 x 16, so
@@ -1014,7 +1015,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   // loop's own and the scheduler can interleave the decode with the MFMAs.
   // Loads past the end repeat the last K-step or pair and are never used.
   auto run = [&](auto nvc) {
-    constexpr int NV = decltype(nvc)::value;
     uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
     BPair bp0, bp1;
     load_a(sa0, 0);
@@ -1235,12 +1235,17 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   constexpr int64_t kOff = int64_t(1) << 31;
   constexpr bool kPairOk = true;
   const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
-  // Weights decoded into registers: whole 128-column h tiles and 256-column y tiles.
-  const bool rb = kRegB && off_ok && q.H % 256 == 0 && q.I % 128 == 0;
-  if (rb)
-    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_rb_kernel<BITS, true, false>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
-             dim3(256), 0, s, a);
-  else if (kPairOk && off_ok && q.H % 128 == 0)
+  // Weights decoded into registers: whole 128-column h tiles and 256-column y
+  // tiles, 2- and 4-bit codes.  3-bit codes stay with the LDS-decode kernel:
+  // measured on one box on the 8,192-token chunk, 650 us against 595 for its
+  // gate/up (2-bit: 453 against 519; 4-bit: 551 against 560).
+  constexpr bool kRbBits = BITS != 3;
+  const bool rb = kRegB && kRbBits && off_ok && q.H % 256 == 0 && q.I % 128 == 0;
+  if (rb) {
+    if constexpr (kRbBits)
+      launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_rb_kernel<BITS, true, false>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
+               dim3(256), 0, s, a);
+  } else if (kPairOk && off_ok && q.H % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk, kNT>,
              dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
@@ -1255,10 +1260,11 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   a.a_zero_row = n;
   a.n_tiles_n = (int)ceil_div(q.H, kBNDown);
   a.out = y;
-  if (rb)
-    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_rb_kernel<BITS, false, YBF16>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
-             dim3(256), 0, s, a);
-  else if (kPairOk && off_ok && q.I % 128 == 0)
+  if (rb) {
+    if constexpr (kRbBits)
+      launch_k(MOE_KERNEL_MFMA_DOWN, mfma_rb_kernel<BITS, false, YBF16>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
+               dim3(256), 0, s, a);
+  } else if (kPairOk && off_ok && q.I % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, kPairOk, kNT>,
              dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
