@@ -33,11 +33,10 @@
 // weights alone already moves outputs by 4e-3 to 9e-3 of their row maximum.
 // Both types run at the same MFMA rate on gfx950.
 //
-// Two kernels.  mfma_rb_kernel (below, used for 2- and 4-bit codes when
-// H % 256 == 0 and I % 128 == 0) decodes each wave's weight rows straight into
-// MFMA operand registers and stages only the activations in LDS;
+// Two kernels.  mfma_rb_kernel (below, used when H % 256 == 0 and I % 128 ==
+// 0) decodes each wave's weight rows straight into MFMA operand registers;
 // mfma_ffn_kernel, described next, decodes the weight tile into LDS and serves
-// 3-bit codes and every other shape.
+// every other shape.
 //
 // Tiling.  Workgroup = 4 waves in a 2 x 2 grid over a BM x BN output tile
 // (128 x 256); each wave owns 64 x 128, i.e. 4 x 8 fragments of 16 x 16, so
@@ -755,16 +754,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
 }
 
 // ---- weights decoded into registers (32 x 32 x 16 MFMA) ------------------------
-// The same GEMMs with the B tile never in LDS.  Each of the 4 waves owns 64
-// of the tile's 256 weight rows for all 128 tile rows: 4 x 2 fragments of
-// v_mfma_f32_32x32x16_f16 (weights as the first operand: D[n][t]).  A lane
-// supplies 8 K-values of one weight row per MFMA, so it decodes those
-// weights itself, straight into the operand registers, from the row's codes
-// and scale/min loaded into registers two K-steps at a time; no two waves
-// decode the same row.  Only the activation tile goes through LDS (8 KB per
-// K-step).  Weight rows are placed so that a lane's 16 outputs of a fragment
-// are 8 consecutive h columns (gate/up: gate and up of each i in the same
-// lane) or 16 consecutive y columns (down): one 16-byte store per 8 values.
+// The same GEMMs with the decoded weight tile never in LDS.  Each of the 4
+// waves owns 64 of the tile's 256 weight rows for all 128 tile rows: 4 x 2
+// fragments of v_mfma_f32_32x32x16_f16 (weights as the first operand:
+// D[n][t]).  A lane supplies 8 K-values of one weight row per MFMA, so it
+// decodes those weights itself, straight into the operand registers, from its
+// row's code words and scale/min word; no two waves decode the same row.  The
+// raw codes and scale/min words reach LDS in 4-K-step chunks loaded as whole
+// 16-byte pieces of each row (half the cache-line accesses of per-lane
+// loads), stored K-step-major; the activation tile goes through LDS as
+// before (8 KB per K-step).  Weight rows are placed so that a lane's 16
+// outputs of a fragment are 8 consecutive h columns (gate/up: gate and up of
+// each i in the same lane) or 16 consecutive y columns (down): one 16-byte
+// store per 8 values.
 //
 // Operand layouts (32 x 32 x 16, f16): lane l gives row l % 32 of the first
 // operand and column l % 32 of the second, K-values 8 (l / 32) .. + 8 of the
@@ -818,6 +820,8 @@ template <int BITS, bool GATEUP, bool YBF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mfma_rb_kernel(GemmArgs A) {
   constexpr int BM = 128, BN = 256, NT = 256, A_CHUNKS = 2;
   __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_bc[2][4][BN * BITS];  // [buffer][K-step][row, word]
+  __shared__ __attribute__((aligned(16))) uint32_t lds_bs[2][4][BN];         // [buffer][K-step][row]
 
   const int xcd = blockIdx.x % kXcd, jb = blockIdx.x / kXcd;
   int tile_idx, nt;
@@ -873,40 +877,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     a_lds[jj] = lds_off_rb(m, ch);
   }
 
-  // ---- this lane's weight rows (one per 32-row fragment fn) ----------------------
-  // fragment row j = lane % 32 = 8 g + 4 hb + r (g < 4, hb, r < 4):
+  // ---- weight rows -------------------------------------------------------------
+  // Tile weight row R = 64 wave + 32 fn + j holds fragment row j of wave
+  // `wave`'s fragment fn; j = 8 g + 4 hb + r (g < 4, hb < 2, r < 4) is
   //   gate/up: plane r >> 1 (gate, up), i = nt*128 + 32*wave + 16*fn + 8*hb + 2*g + (r & 1)
   //   down:    n = nt*256 + 64*wave + 32*fn + 16*hb + 4*g + r
+  // (rows past I or H read row 0; their outputs are never stored).
   const int64_t row_code_bytes = (int64_t)K * BITS / 8, row_sm_bytes = (int64_t)(K / 32) * 4;
-  int bc_voff[2], bs_voff[2];
-  {
-    const int g = jl >> 3, hb = (jl >> 2) & 1, r = jl & 3;
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn) {
-      int64_t row, oc, os;
-      if constexpr (GATEUP) {
-        const int i = nt * (BN / 2) + 32 * wave + 16 * fn + 8 * hb + 2 * g + (r & 1);
-        row = i < A.I ? i : 0;
-        oc = (r >> 1) ? A.off_c1 : A.off_c0;
-        os = (r >> 1) ? A.off_s1 : A.off_s0;
-      } else {
-        const int n = nt * BN + 64 * wave + 32 * fn + 16 * hb + 4 * g + r;
-        row = n < A.H ? n : 0;
-        oc = A.off_c0;
-        os = A.off_s0;
-      }
-      bc_voff[fn] = (int)(oc + row * row_code_bytes);
-      bs_voff[fn] = (int)(os + row * row_sm_bytes);
+  auto row_offsets = [&](int R, int& code_off, int& sm_off) {
+    const int w = R >> 6, fn = (R >> 5) & 1, j = R & 31;
+    const int g = j >> 3, hb = (j >> 2) & 1, r = j & 3;
+    int64_t row, oc, os;
+    if constexpr (GATEUP) {
+      const int i = nt * (BN / 2) + 32 * w + 16 * fn + 8 * hb + 2 * g + (r & 1);
+      row = i < A.I ? i : 0;
+      oc = (r >> 1) ? A.off_c1 : A.off_c0;
+      os = (r >> 1) ? A.off_s1 : A.off_s0;
+    } else {
+      const int n = nt * BN + 64 * w + 32 * fn + 16 * hb + 4 * g + r;
+      row = n < A.H ? n : 0;
+      oc = A.off_c0;
+      os = A.off_s0;
     }
+    code_off = (int)(oc + row * row_code_bytes);
+    sm_off = (int)(os + row * row_sm_bytes);
+  };
+  // The weight codes and scale/min words go through LDS in chunks of 4
+  // K-steps: each row's 16 BITS bytes of codes and 16 bytes of scale/min per
+  // chunk are loaded as whole 16-byte pieces (consecutive threads on
+  // consecutive pieces of a row) and stored K-step-major, [K-step][row], so a
+  // wave's 32 rows of one K-step are one contiguous run when the lanes read
+  // their own row's words.  Thread t loads code pieces t + 256 i (i < BITS) and
+  // the scale/min piece of row t.
+  constexpr int CK = 4;
+  int bc_goff[BITS], bc_row[BITS], bc_piece[BITS], bs_goff;
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) {
+    const int pc = tid + NT * i;
+    bc_row[i] = pc / BITS;
+    bc_piece[i] = pc % BITS;
+    int co, so;
+    row_offsets(bc_row[i], co, so);
+    bc_goff[i] = co + 16 * bc_piece[i];
+  }
+  {
+    int co;
+    row_offsets(tid, co, bs_goff);
   }
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(A.a_src), (short)0, kBufRecords, kBufFlags);
   const __amdgpu_buffer_rsrc_t rsb =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob), (short)0, kBufRecords, kBufFlags);
 
-  struct BPair {  // two K-steps of both rows: codes (BITS words per K-step) and scale/min words
-    uint32_t w[2][2 * BITS];
-    uint2 sm[2];
+  struct BStage {  // this thread's pieces of one chunk
+    uint4 c[BITS];
+    uint4 s;
+  };
+  struct BStep {  // one K-step of this lane's two rows: codes and scale/min word
+    uint32_t w[2][BITS];
+    uint32_t sm[2];
   };
   auto load_a = [&](uint4 (&a)[A_CHUNKS], int ks) {
 #pragma unroll
@@ -917,29 +946,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
     for (int jj = 0; jj < A_CHUNKS; ++jj) *reinterpret_cast<uint4*>(&lds_a[buf][a_lds[jj]]) = a[jj];
   };
-  auto load_bpair = [&](BPair& bp, int ks) {  // ks even, ks + 1 < KS
+  auto load_bchunk = [&](BStage& st, int kc) {  // kc: the chunk's first K-step, kc + CK <= KS
+#pragma unroll
+    for (int i = 0; i < BITS; ++i)
+      st.c[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bc_goff[i], kc * (4 * BITS), 0));
+    st.s = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bs_goff, kc * 4, 0));
+  };
+  auto store_bchunk = [&](const BStage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) {
+      const uint32_t v[4] = {st.c[i].x, st.c[i].y, st.c[i].z, st.c[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int wi = 4 * bc_piece[i] + q;  // word of the row's chunk: K-step wi / BITS, word wi % BITS
+        lds_bc[buf][wi / BITS][bc_row[i] * BITS + wi % BITS] = v[q];
+      }
+    }
+    lds_bs[buf][0][tid] = st.s.x;
+    lds_bs[buf][1][tid] = st.s.y;
+    lds_bs[buf][2][tid] = st.s.z;
+    lds_bs[buf][3][tid] = st.s.w;
+  };
+  auto read_bstep = [&](BStep& bs, int buf, int ksl) {
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
-      if constexpr (BITS == 3) {
+      const int R = 64 * wave + 32 * fn + jl;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          const uint2 v = __builtin_bit_cast(
-              uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bc_voff[fn] + 8 * j, ks * (4 * BITS), 0));
-          bp.w[fn][2 * j] = v.x;
-          bp.w[fn][2 * j + 1] = v.y;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < BITS / 2; ++j) {
-          const uint4 v = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bc_voff[fn] + 16 * j, ks * (4 * BITS), 0));
-          bp.w[fn][4 * j] = v.x;
-          bp.w[fn][4 * j + 1] = v.y;
-          bp.w[fn][4 * j + 2] = v.z;
-          bp.w[fn][4 * j + 3] = v.w;
-        }
-      }
-      bp.sm[fn] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsb, bs_voff[fn], ks * 4, 0));
+      for (int w = 0; w < BITS; ++w) bs.w[fn][w] = lds_bc[buf][ksl][R * BITS + w];
+      bs.sm[fn] = lds_bs[buf][ksl][R];
     }
   };
 
@@ -952,21 +986,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
       for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
 
   // ---- the K-step pieces -------------------------------------------------------
-  // Tables of K-step e of pair bp for this lane's two rows.
-  auto tables = [&](const BPair& bp, int e, Lut2 (&t)[2], Dec16 (&d)[2]) {
+  auto tables = [&](const BStep& bs, Lut2 (&t)[2], Dec16 (&d)[2]) {
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
-      const uint32_t smw = e ? bp.sm[fn].y : bp.sm[fn].x;
-      if constexpr (BITS == 2) t[fn] = lut2(smw);
-      else d[fn] = dec16(smw);
+      if constexpr (BITS == 2) t[fn] = lut2(bs.sm[fn]);
+      else d[fn] = dec16(bs.sm[fn]);
     }
   };
-  // Weight operands of K-half kh of K-step e of pair bp.
-  auto dec_half = [&](const BPair& bp, int e, int kh, const Lut2 (&t)[2], const Dec16 (&d)[2], f16x8_t (&bo)[2]) {
+  auto dec_half = [&](const BStep& bs, int kh, const Lut2 (&t)[2], const Dec16 (&d)[2], f16x8_t (&bo)[2]) {
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
       uint32_t o[4];
-      dec8<BITS>(bp.w[fn] + e * BITS, kh, hh, t[fn], d[fn], o);
+      dec8<BITS>(bs.w[fn], kh, hh, t[fn], d[fn], o);
       bo[fn] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
@@ -1007,62 +1038,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 
   // Pipeline: activation chunks two K-steps ahead in registers (sa0 even
   // stages, sa1 odd), LDS double-buffered with one barrier per K-step; weight
-  // pairs bp0 (stages 4j, 4j+1) and bp1 (4j+2, 4j+3) loaded two K-steps
-  // before their first use.  A K-half's operands (activation fragments from
-  // LDS, weights decoded from the pair registers) are prepared under the
+  // chunks (4 K-steps) loaded into registers three K-steps before they are
+  // stored to their LDS buffer (double-buffered, stored one K-step before
+  // their first use).  A K-half's operands (activation fragments and this
+  // lane's weight words from LDS, weights decoded) are prepared under the
   // MFMAs of the K-half before.  For 2-bit codes the loop is specialised on
   // the number of filled fragment rows (nv), so that it has no branch but the
   // loop's own and the scheduler can interleave the decode with the MFMAs.
-  // Loads past the end repeat the last K-step or pair and are never used.
+  // Loads past the end repeat the last K-step or chunk and are never used.
   auto run = [&](auto nvc) {
     uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
-    BPair bp0, bp1;
+    BStage st;
     load_a(sa0, 0);
     load_a(sa1, min(1, KS - 1));
-    load_bpair(bp0, 0);
-    load_bpair(bp1, 2);
+    load_bchunk(st, 0);
     store_a(sa0, 0);
+    store_bchunk(st, 0);
     __syncthreads();
     load_a(sa0, min(2, KS - 1));
+    load_bchunk(st, min(CK, KS - CK));
     f16x8_t ao0[4], ao1[4], bo[2], bo2[2];
     Lut2 t[2] = {};
     Dec16 d[2] = {};
+    BStep cs, ns;
     read_a(0, 0, ao0);
-    tables(bp0, 0, t, d);
-    dec_half(bp0, 0, 0, t, d, bo);
+    read_bstep(cs, 0, 0);
+    tables(cs, t, d);
+    dec_half(cs, 0, t, d, bo);
     __builtin_amdgcn_sched_barrier(0);
-    // One K-step (LDS buffer `buf`) on pair `cur` (its K-step ec); `nxt`, en:
-    // the next K-step's pair; a_next: the next K-step's activation chunks.
-    auto step = [&](int buf, const BPair& cur, int ec, const BPair& nxt, int en, const uint4 (&a_next)[A_CHUNKS]) {
+    // One K-step (activation buffer `buf`); the next K-step's weights are
+    // K-step nksl of weight buffer nbb; `pre` runs before the barrier.
+    auto step = [&](int buf, int nbb, int nksl, const uint4 (&a_next)[A_CHUNKS], auto&& pre) {
       mfma_half(nvc, bo, ao0, [&] {
         read_a(buf, 1, ao1);
-        dec_half(cur, ec, 1, t, d, bo2);
+        dec_half(cs, 1, t, d, bo2);
       });
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(nvc, bo2, ao1, [&] {
-        tables(nxt, en, t, d);
-        dec_half(nxt, en, 0, t, d, bo);
+        read_bstep(ns, nbb, nksl);
+        tables(ns, t, d);
+        dec_half(ns, 0, t, d, bo);
       });
       __builtin_amdgcn_sched_barrier(0);
       store_a(a_next, buf ^ 1);
+      pre();
       __syncthreads();
       read_a(buf ^ 1, 0, ao0);
+      cs = ns;
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int kb = 0; kb < KS; kb += 4) {
-      step(0, bp0, 0, bp0, 1, sa1);  // stage kb (sa1: stage kb + 1)
+      const int bb = (kb / CK) & 1;
+      step(0, bb, 1, sa1, [] {});  // stage kb (sa1: stage kb + 1)
       load_a(sa1, min(kb + 3, KS - 1));
       __builtin_amdgcn_sched_barrier(0);
-      step(1, bp0, 1, bp1, 0, sa0);  // stage kb + 1 (sa0: stage kb + 2)
+      step(1, bb, 2, sa0, [] {});  // stage kb + 1 (sa0: stage kb + 2)
       load_a(sa0, min(kb + 4, KS - 1));
-      load_bpair(bp0, min(kb + 4, KS - 2));
       __builtin_amdgcn_sched_barrier(0);
-      step(0, bp1, 0, bp1, 1, sa1);  // stage kb + 2
+      step(0, bb, 3, sa1, [&] { store_bchunk(st, bb ^ 1); });  // stage kb + 2; the next chunk into LDS
       load_a(sa1, min(kb + 5, KS - 1));
       __builtin_amdgcn_sched_barrier(0);
-      step(1, bp1, 1, bp0, 0, sa0);  // stage kb + 3
+      step(1, bb ^ 1, 0, sa0, [] {});  // stage kb + 3
       load_a(sa0, min(kb + 6, KS - 1));
-      load_bpair(bp1, min(kb + 6, KS - 2));
+      load_bchunk(st, min(kb + 2 * CK, KS - CK));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1235,17 +1273,15 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   constexpr int64_t kOff = int64_t(1) << 31;
   constexpr bool kPairOk = true;
   const bool off_ok = (int64_t)(T + 1) * q.H * 2 < kOff && (int64_t)(n + 1) * q.I * 2 < kOff && q.stride < kOff;
-  // Weights decoded into registers: whole 128-column h tiles and 256-column y
-  // tiles, 2- and 4-bit codes.  3-bit codes stay with the LDS-decode kernel:
-  // measured on one box on the 8,192-token chunk, 650 us against 595 for its
-  // gate/up (2-bit: 453 against 519; 4-bit: 551 against 560).
-  constexpr bool kRbBits = BITS != 3;
-  const bool rb = kRegB && kRbBits && off_ok && q.H % 256 == 0 && q.I % 128 == 0;
-  if (rb) {
-    if constexpr (kRbBits)
-      launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_rb_kernel<BITS, true, false>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
-               dim3(256), 0, s, a);
-  } else if (kPairOk && off_ok && q.H % 128 == 0)
+  // Weights decoded into registers for whole 128-column h tiles and 256-column
+  // y tiles.  On the 8,192-token chunk its gate/up took 408, 514 and 470 us
+  // for 2-, 3- and 4-bit codes against 519, 594 and 560 for the LDS-decode
+  // kernel (one box, Zipf(1.1) routing).
+  const bool rb = kRegB && off_ok && q.H % 256 == 0 && q.I % 128 == 0;
+  if (rb)
+    launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_rb_kernel<BITS, true, false>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
+             dim3(256), 0, s, a);
+  else if (kPairOk && off_ok && q.H % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_GATEUP, mfma_ffn_kernel<BITS, kBM, kBNGateUp, true, false, kPairOk, kNT>,
              dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
@@ -1260,11 +1296,10 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
   a.a_zero_row = n;
   a.n_tiles_n = (int)ceil_div(q.H, kBNDown);
   a.out = y;
-  if (rb) {
-    if constexpr (kRbBits)
-      launch_k(MOE_KERNEL_MFMA_DOWN, mfma_rb_kernel<BITS, false, YBF16>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
-               dim3(256), 0, s, a);
-  } else if (kPairOk && off_ok && q.I % 128 == 0)
+  if (rb)
+    launch_k(MOE_KERNEL_MFMA_DOWN, mfma_rb_kernel<BITS, false, YBF16>, dim3((unsigned)(tiles_pad * a.n_tiles_n)),
+             dim3(256), 0, s, a);
+  else if (kPairOk && off_ok && q.I % 128 == 0)
     launch_k(MOE_KERNEL_MFMA_DOWN, mfma_ffn_kernel<BITS, kBM, kBNDown, false, YBF16, kPairOk, kNT>,
              dim3((unsigned)(tiles_pad * a.n_tiles_n)), dim3(kNT), 0, s, a);
   else
