@@ -50,13 +50,15 @@ ROUNDS = 3  # timed rounds per measurement; the value is their median
 
 # Memory traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two runs), scaled
 # by what the same counters read for a plain 256 MiB device-to-device copy in the same runs (FETCH_SIZE reads
-# 131,093.5 KiB for it: x1.99968; WRITE_SIZE reads 262,144 KiB: x1.0).  Each entry is valid only for the kernel
+# 131,093.4 KiB for it: x1.99970; WRITE_SIZE reads 262,144 KiB: x1.0).  Each entry is valid only for the kernel
 # sources it was measured on (first 16 hex digits of their SHA-256); after a change the traffic is reported null.
-FETCH_SCALE = 262144.0 / 131093.5
+FETCH_SCALE = 262144.0 / 131093.4
 WRITE_SCALE = 1.0
 TRAFFIC = {
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "d4fdb911b67e081d", "fetch_kib": 297229.0,
-                    "write_kib": 83621.0},
+    "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp", "slot_dev.hpp"],
+                    "sha": "e4fc07354f2fefb9", "fetch_kib": 7625.125, "write_kib": 62.9375},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "55b81e9dd96d6abd", "fetch_kib": 291166.6875,
+                    "write_kib": 81928.875},
 }
 
 
