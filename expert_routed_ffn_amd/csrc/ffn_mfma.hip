@@ -1042,9 +1042,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   // stored to their LDS buffer (double-buffered, stored one K-step before
   // their first use).  A K-half's operands (activation fragments and this
   // lane's weight words from LDS, weights decoded) are prepared under the
-  // MFMAs of the K-half before.  For 2-bit codes the loop is specialised on
-  // the number of filled fragment rows (nv), so that it has no branch but the
-  // loop's own and the scheduler can interleave the decode with the MFMAs.
+  // MFMAs of the K-half before.  For 2- and 4-bit codes the loop is
+  // specialised on the number of filled fragment rows (nv), so that it has no
+  // branch but the loop's own and the scheduler can interleave the decode
+  // with the MFMAs.
   // Loads past the end repeat the last K-step or chunk and are never used.
   auto run = [&](auto nvc) {
     uint4 sa0[A_CHUNKS], sa1[A_CHUNKS];
@@ -1104,7 +1105,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  if constexpr (BITS == 2) {  // the specialised loops fit the register budget for 2-bit codes only
+  if constexpr (BITS != 3) {  // the specialised loops spill for 3-bit codes
     switch (nv) {
       case 1: run(std::integral_constant<int, 1>{}); break;
       case 2: run(std::integral_constant<int, 2>{}); break;
