@@ -57,8 +57,8 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp", "slot_dev.hpp"],
                     "sha": "e4fc07354f2fefb9", "fetch_kib": 7625.125, "write_kib": 62.9375},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "55b81e9dd96d6abd", "fetch_kib": 291166.6875,
-                    "write_kib": 81928.875},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "97258290322155e1", "fetch_kib": 291176.9375,
+                    "write_kib": 81928.53125},
 }
 
 
