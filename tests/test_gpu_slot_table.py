@@ -303,3 +303,66 @@ def test_layer_decode_slots_matches_resident_layer_decode(moe, bits, T, n_slots,
     for t in tables:
         t.close()
     _check_against_oracle(w, host, rec)
+
+
+def test_layer_decode_slots_table_above_register_stamps(moe):
+    """A table of 4,160 slots, more than the in-launch resolve holds in registers (256 threads x 16 stamps),
+    so its victim search reads the stamps from memory.  Preload fills every slot, the experts of the two
+    computed layers first (oldest, the most popular among them), so misses evict, and the most popular
+    experts are the oldest: a hit among them must not be taken as a victim in the same resolve.  Outputs
+    bit-identical to resident weights, map and counters equal to those of the stand-alone device resolve,
+    filled slots of the computed layers hold their blobs, and the oracle agrees."""
+    import torch
+    L, E, n_slots, run = 33, 128, 4160, 2
+    assert n_slots > 256 * 16 and n_slots <= L * E
+    w = synth.Workload("large_table", E=E, k=10, H=2048, I=512, T=3, bits=2, x_dtype="bf16", zipf_s=1.2, layers=L)
+    eb = w.expert_bytes
+    host = torch.empty(L * E * eb, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy().reshape(L, E, eb)
+    for l in range(run):
+        synth.layer_experts(w.seed, l, E, w.H, w.I, w.bits, out=hv[l])
+    hv[run:] = 0  # layers never computed: their blobs are only placed and copied
+    dev_run = host[: run * E * eb].to("cuda")
+    resident = [moe.ExpertLayer(E, w.H, w.I, w.bits, dev_run, eb, base_offset=l * E * eb) for l in range(run)]
+    pairs = []
+    for l in range(run):  # by popularity, ranks 8..39 left out so that they miss
+        order = np.argsort(-w.bias(l), kind="stable")
+        pairs += [(l, int(e)) for e in np.concatenate([order[:8], order[40:]])]
+    pairs += [(l, e) for l in range(run, L) for e in range(E)]
+    assert len(pairs) == n_slots
+    tables = []
+    for _ in range(2):
+        slots = torch.empty(n_slots * eb, dtype=torch.uint8, device="cuda")
+        smap = torch.empty(L * E, dtype=torch.int32, device="cuda")
+        t = moe.SlotTable(L, E, n_slots, eb, host, slots, smap)
+        t.preload(pairs)
+        t.enable_device()
+        tables.append(t)
+    fused, split = tables
+    rec = []
+    for s in range(3):
+        x = torch.from_numpy(w.x(0, s).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        for l in range(run):
+            lg = torch.from_numpy(synth.logits(synth.stream_key(w.seed, synth.TAG_LOGITS, l, s), w.T, E,
+                                               synth.drifted_bias(w, l, s, 0.05))).cuda()
+            a = moe.layer_decode(resident[l], x, lg, w.k, residual=x)
+            b = moe.layer_decode_slots(fused, l, fused.layer(l, w.H, w.I, w.bits), x, lg, w.k, residual=x)
+            split.resolve_device(l, moe.dispatch(a[0], E))
+            torch.cuda.synchronize()
+            for u, v in zip((a[0], a[1], a[3], a[4]), (b[0], b[1], b[3], b[4])):
+                assert np.array_equal(to_host(u).view(np.uint32), to_host(v).view(np.uint32)), (s, l)
+            rec.append((l, x.view(torch.int16).cpu().numpy().view(np.uint16).copy(), to_host(lg).copy(),
+                        to_host(b[4]).copy()))
+            x = a[4].to(torch.bfloat16)
+    st = fused.stats()
+    assert st == split.stats()
+    assert np.array_equal(fused.map_host(), split.map_host())
+    assert st["misses"] > 0 and st["evictions"] > 0, st
+    smap = fused.map_host().reshape(-1)
+    filled = np.flatnonzero(smap[: run * E] >= 0)
+    got = fused.slots.view(n_slots, eb)[torch.from_numpy(smap[filled].astype(np.int64)).cuda()].cpu().numpy()
+    assert np.array_equal(got, host.numpy().reshape(L * E, eb)[filled])
+    assert (smap >= 0).sum() == n_slots
+    for t in tables:
+        t.close()
+    _check_against_oracle(w, host, rec)
