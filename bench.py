@@ -361,8 +361,7 @@ def prefill_bench(args, torch, moe, synth, oracle, bits: int = 2, bias: float | 
             "unit": "TFLOP/s",
             "frac": gu_flops / (gu_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "traffic": measured_traffic("mfma_gateup") if bits == 2 and bias == 1.0 else None,
-            "kernel": ("mfma_ffn_kernel gate/up (fp16 16x16x32 MFMA, weights decoded in LDS)" if bits == 3 else
-                       "mfma_rb_kernel gate/up (fp16 32x32x16 MFMA, weights decoded into registers)"),
+            "kernel": "mfma_rb_kernel gate/up (fp16 32x32x16 MFMA, weights decoded into registers)",
             "flops_per_launch": gu_flops,
             "mean_us": gu_ms * 1e3,
             "down_mean_us": dn_ms * 1e3,
