@@ -778,14 +778,18 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // each bank once per 16 lanes.
 __device__ __forceinline__ int lds_off_rb(int row, int chunk) { return row * kPitch + ((chunk ^ ((row >> 2) & 3)) * 8); }
 
-// The 2-bit table of one (row, block): entries fp16_rne(fp32 fma(s, q, m)), q = 0..3.
-struct Lut2 {
-  uint32_t lo, hi;
-};
-__device__ __forceinline__ Lut2 lut2(uint32_t smw) {
-  const float s = f16lo(smw), m = f16hi(smw);
-  return Lut2{pack_f16(__builtin_fmaf(s, 0.f, m), __builtin_fmaf(s, 1.f, m)),
-              pack_f16(__builtin_fmaf(s, 2.f, m), __builtin_fmaf(s, 3.f, m))};
+// Codes decoded in place: the pair of codes at bits p / 16 + p (mask: the
+// code's bits at 0 / 16) is masked out of the word unshifted and ORed into
+// fp16 2^(10 - p), whose mantissa bit p is worth 1, so each half reads
+// 2^(10 - p) + q exactly (p + code width <= 10); subtracting 2^(10 - p)
+// leaves q, and one packed fma gives fp16(s q + m) with a single rounding.
+template <int P, uint32_t MASK>
+__device__ __forceinline__ uint32_t dec_pair_at(uint32_t w, const Dec16& d) {
+  static_assert(P >= 0 && P <= 10, "code inside the fp16 mantissa");
+  constexpr uint32_t e = 0x6400u - 0x0400u * P;  // fp16 bits of 2^(10 - P)
+  const _Float16 base = __builtin_bit_cast(_Float16, (uint16_t)e);
+  const f16x2_t q = __builtin_bit_cast(f16x2_t, and_or(w, MASK << P, e | (e << 16))) - f16x2_t{base, base};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d.s2, d.m2));
 }
 
 // 8 weights (4 packed pairs) of one row for K-half kh of a K-step, lane half
@@ -793,15 +797,13 @@ __device__ __forceinline__ Lut2 lut2(uint32_t smw) {
 // words (2-bit: one per 16 weights; 3-bit: low bits of each half, then the
 // high-bit word; 4-bit: two per 16 weights).
 template <int BITS>
-__device__ __forceinline__ void dec8(const uint32_t* c, int kh, int hh, const Lut2& t, const Dec16& d,
-                                     uint32_t (&o)[4]) {
+__device__ __forceinline__ void dec8(const uint32_t* c, int kh, int hh, const Dec16& d, uint32_t (&o)[4]) {
   if constexpr (BITS == 2) {
     const uint32_t w = c[kh] >> (8 * hh);  // pairs 4 hh .. 4 hh + 3 at bits 2j / 16 + 2j
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t q2 = (w >> (2 * j)) & 0x00030003u;
-      o[j] = __builtin_amdgcn_perm(t.hi, t.lo, q2 * 0x0202u + 0x01000100u);
-    }
+    o[0] = dec_pair_at<0, 0x00030003u>(w, d);
+    o[1] = dec_pair_at<2, 0x00030003u>(w, d);
+    o[2] = dec_pair_at<4, 0x00030003u>(w, d);
+    o[3] = dec_pair_at<6, 0x00030003u>(w, d);
   } else if constexpr (BITS == 3) {
     const uint32_t lo = c[kh] >> (8 * hh), hi = (c[2] >> (8 * kh)) >> (4 * hh);
 #pragma unroll
@@ -810,9 +812,11 @@ __device__ __forceinline__ void dec8(const uint32_t* c, int kh, int hh, const Lu
       o[j] = dec_pair(and_or(lo >> (2 * j), 0x00030003u, 0x64006400u | h2), d);
     }
   } else {
-    const uint32_t w = hh ? c[2 * kh + 1] : c[2 * kh];  // pairs at bits 4j / 16 + 4j
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = dec_pair(and_or(w >> (4 * j), 0x000F000Fu, 0x64006400u), d);
+    const uint32_t w = hh ? c[2 * kh + 1] : c[2 * kh], w8 = w >> 8;  // pairs at bits 4j / 16 + 4j
+    o[0] = dec_pair_at<0, 0x000F000Fu>(w, d);
+    o[1] = dec_pair_at<4, 0x000F000Fu>(w, d);
+    o[2] = dec_pair_at<0, 0x000F000Fu>(w8, d);
+    o[3] = dec_pair_at<4, 0x000F000Fu>(w8, d);
   }
 }
 
@@ -986,18 +990,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
       for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
 
   // ---- the K-step pieces -------------------------------------------------------
-  auto tables = [&](const BStep& bs, Lut2 (&t)[2], Dec16 (&d)[2]) {
+  auto tables = [&](const BStep& bs, Dec16 (&d)[2]) {
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn) {
-      if constexpr (BITS == 2) t[fn] = lut2(bs.sm[fn]);
-      else d[fn] = dec16(bs.sm[fn]);
-    }
+    for (int fn = 0; fn < 2; ++fn) d[fn] = dec16(bs.sm[fn]);
   };
-  auto dec_half = [&](const BStep& bs, int kh, const Lut2 (&t)[2], const Dec16 (&d)[2], f16x8_t (&bo)[2]) {
+  auto dec_half = [&](const BStep& bs, int kh, const Dec16 (&d)[2], f16x8_t (&bo)[2]) {
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
       uint32_t o[4];
-      dec8<BITS>(bs.w[fn], kh, hh, t[fn], d[fn], o);
+      dec8<BITS>(bs.w[fn], kh, hh, d[fn], o);
       bo[fn] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
@@ -1059,26 +1060,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     load_a(sa0, min(2, KS - 1));
     load_bchunk(st, min(CK, KS - CK));
     f16x8_t ao0[4], ao1[4], bo[2], bo2[2];
-    Lut2 t[2] = {};
     Dec16 d[2] = {};
     BStep cs, ns;
     read_a(0, 0, ao0);
     read_bstep(cs, 0, 0);
-    tables(cs, t, d);
-    dec_half(cs, 0, t, d, bo);
+    tables(cs, d);
+    dec_half(cs, 0, d, bo);
     __builtin_amdgcn_sched_barrier(0);
     // One K-step (activation buffer `buf`); the next K-step's weights are
     // K-step nksl of weight buffer nbb; `pre` runs before the barrier.
     auto step = [&](int buf, int nbb, int nksl, const uint4 (&a_next)[A_CHUNKS], auto&& pre) {
       mfma_half(nvc, bo, ao0, [&] {
         read_a(buf, 1, ao1);
-        dec_half(cs, 1, t, d, bo2);
+        dec_half(cs, 1, d, bo2);
       });
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(nvc, bo2, ao1, [&] {
         read_bstep(ns, nbb, nksl);
-        tables(ns, t, d);
-        dec_half(ns, 0, t, d, bo);
+        tables(ns, d);
+        dec_half(ns, 0, d, bo);
       });
       __builtin_amdgcn_sched_barrier(0);
       store_a(a_next, buf ^ 1);
