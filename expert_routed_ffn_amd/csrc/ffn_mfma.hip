@@ -792,6 +792,19 @@ __device__ __forceinline__ uint32_t dec_pair_at(uint32_t w, const Dec16& d) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d.s2, d.m2));
 }
 
+// 3-bit codes in place: pair J's low bits at 2J / 16 + 2J of `lo`, its high
+// bits at J / 16 + J of `hi`; hi << (J + 2) puts them at 2J + 2, above the
+// low bits, and the three bits decode as in dec_pair_at with p = 2J.
+template <int J>
+__device__ __forceinline__ uint32_t dec_pair3_at(uint32_t lo, uint32_t hi, const Dec16& d) {
+  constexpr int P = 2 * J;
+  constexpr uint32_t e = 0x6400u - 0x0400u * P;  // fp16 bits of 2^(10 - P)
+  const _Float16 base = __builtin_bit_cast(_Float16, (uint16_t)e);
+  const uint32_t t = and_or(hi << (J + 2), 0x00040004u << P, e | (e << 16));
+  const f16x2_t q = __builtin_bit_cast(f16x2_t, and_or(lo, 0x00030003u << P, t)) - f16x2_t{base, base};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, d.s2, d.m2));
+}
+
 // 8 weights (4 packed pairs) of one row for K-half kh of a K-step, lane half
 // hh = l / 32 (weights 16 kh + 8 hh .. + 8 of the block).  c: the K-step's code
 // words (2-bit: one per 16 weights; 3-bit: low bits of each half, then the
@@ -806,11 +819,10 @@ __device__ __forceinline__ void dec8(const uint32_t* c, int kh, int hh, const De
     o[3] = dec_pair_at<6, 0x00030003u>(w, d);
   } else if constexpr (BITS == 3) {
     const uint32_t lo = c[kh] >> (8 * hh), hi = (c[2] >> (8 * kh)) >> (4 * hh);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t h2 = ((hi >> j) & 0x00010001u) << 2;
-      o[j] = dec_pair(and_or(lo >> (2 * j), 0x00030003u, 0x64006400u | h2), d);
-    }
+    o[0] = dec_pair3_at<0>(lo, hi, d);
+    o[1] = dec_pair3_at<1>(lo, hi, d);
+    o[2] = dec_pair3_at<2>(lo, hi, d);
+    o[3] = dec_pair3_at<3>(lo, hi, d);
   } else {
     const uint32_t w = hh ? c[2 * kh + 1] : c[2 * kh], w8 = w >> 8;  // pairs at bits 4j / 16 + 4j
     o[0] = dec_pair_at<0, 0x000F000Fu>(w, d);
