@@ -120,6 +120,13 @@ __device__ __forceinline__ float swiglu_scaled(float g, float u, int ex) {
   const float en = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
   return g * __builtin_amdgcn_rcpf(1.0f + en) * u;
 }
+// The same with cz = -log2(e) * 2^e_t formed once per row: g * cz rounds
+// exactly as (g * 2^e_t) * -log2(e) does, a power of two commuting with the
+// rounding (barring overflow and subnormals).
+__device__ __forceinline__ float swiglu_c(float g, float u, float cz) {
+  const float en = __builtin_amdgcn_exp2f(g * cz);
+  return g * __builtin_amdgcn_rcpf(1.0f + en) * u;
+}
 
 __device__ __forceinline__ float f16lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
@@ -1138,23 +1145,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
       // 2^-e_t times their true values: h' = g' * sigmoid(g' * 2^e_t) * u' = h * 2^(-2 e_t)
       _Float16* hrow = reinterpret_cast<_Float16*>(A.out) + (size_t)(p_begin + m) * A.I;
       const int ex = A.xexp[A.sorted_assign[p_begin + m] / A.k];
-      int sat = 0;
+      const float cz = __builtin_amdgcn_ldexpf(-1.4426950408889634f, ex);  // -log2(e) 2^e_t, exact
+      float h[2][8], mx = 0.f;
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& v = acc[fm][fn];
+          h[fn][2 * g] = swiglu_c(v[4 * g], v[4 * g + 2], cz);
+          h[fn][2 * g + 1] = swiglu_c(v[4 * g + 1], v[4 * g + 3], cz);
+          mx = fmaxf(mx, fmaxf(fabsf(h[fn][2 * g]), fabsf(h[fn][2 * g + 1])));
+        }
+      if (mx > kF16Max) {  // rare: count the values past fp16 range and clamp them
+        int sat = 0;
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            sat += fabsf(h[fn][q]) > kF16Max;
+            h[fn][q] = sat_f16(h[fn][q]);
+          }
+        atomicAdd(A.clip, (uint32_t)sat);
+      }
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn) {
         const int i0 = nt * (BN / 2) + 32 * wave + 16 * fn + 8 * hh;
-        const f32x16_t v = acc[fm][fn];
-        uint32_t pk[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float g0 = v[4 * g], g1 = v[4 * g + 1], u0 = v[4 * g + 2], u1 = v[4 * g + 3];
-          const float h0 = swiglu_scaled(g0, u0, ex);
-          const float h1 = swiglu_scaled(g1, u1, ex);
-          sat += (fabsf(h0) > kF16Max) + (fabsf(h1) > kF16Max);
-          pk[g] = pack_f16(sat_f16(h0), sat_f16(h1));
-        }
-        *reinterpret_cast<uint4*>(hrow + i0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        *reinterpret_cast<uint4*>(hrow + i0) =
+            make_uint4(pack_f16(h[fn][0], h[fn][1]), pack_f16(h[fn][2], h[fn][3]), pack_f16(h[fn][4], h[fn][5]),
+                       pack_f16(h[fn][6], h[fn][7]));
       }
-      if (sat) atomicAdd(A.clip, (uint32_t)sat);
     } else {
       const int64_t a = A.sorted_assign[p_begin + m];
       const int ey = 2 * A.xexp[a / A.k];
