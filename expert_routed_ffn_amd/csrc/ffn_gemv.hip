@@ -240,6 +240,27 @@ template <int TM> constexpr int kRLGateUp = TM >= 4 ? MOE_RL_GU_4 : TM == 3 ? MO
 template <int TM> constexpr int kRLGateUpSplit = TM >= 3 ? 4 : 8;
 template <int TM> constexpr int kRLDown = TM >= 4 ? MOE_RL_DN_4 : TM == 3 ? MOE_RL_DN_3 : MOE_RL_DN_1;
 
+// Brings every 64-byte line of the first BYTES bytes of the kernel-argument
+// segment into the scalar cache with one round trip.  The decode kernels' large
+// argument structs and their scalar register pressure make the compiler load
+// arguments where they are first used and wait after each load, so a workgroup
+// otherwise pays several dependent cache misses before its first memory access.
+// The words read are discarded; every read lies inside the segment.
+#ifndef MOE_WARM_KERNARGS
+#define MOE_WARM_KERNARGS 1
+#endif
+template <int BYTES>
+__device__ __forceinline__ void warm_kernargs() {
+  if constexpr (MOE_WARM_KERNARGS != 0) {
+    typedef __attribute__((address_space(4))) const uint32_t kword_t;
+    kword_t* k = (kword_t*)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t d = 0;
+#pragma unroll
+    for (int off = 64; off + 4 <= BYTES; off += 64) d ^= k[off / 4];
+    asm volatile("" ::"s"(d));
+  }
+}
+
 struct DecodeArgs {
   const uint8_t* base;
   int64_t stride;
@@ -836,109 +857,114 @@ __device__ __forceinline__ void stage_copy_list(const StageArgs& G, int nc, cons
 }
 
 // ---- row-tiled down with the combine folded in ------------------------------------
-// One 1024-thread workgroup owns kRowTile output rows of H.  Its 16 waves take
-// the routed rows (sorted positions: one expert and one assignment each), up
-// to two at a time per wave, over the tile's rows (two steps of 4 rows, 16
-// lanes per row); the y values of the tile go to global memory and to LDS, and
-// the workgroup then forms out[t] = residual[t] + sum_j w[t,j] y[t,j] for its
-// rows with the same fused multiply-add chain as the combine kernel.  No
-// workgroup depends on another.
-constexpr int kRowTile = 8;
-constexpr int kRowWaves = 16;
+// One workgroup of kRowWaves waves owns kRowTile (8) output rows of H.  A wave
+// takes four routed rows (sorted positions, one expert and one assignment
+// each) at a time, 16 lanes per position: each lane reads its 32-column chunk
+// of the position's h row once and the same chunk of the tile's rows of the
+// position's down matrix, and the 16 lanes of a position then reduce the row
+// sums together (a lane reading h for one position only, where lanes taking
+// different rows of one position read the same h chunk four times over).  The
+// y values of the tile go to global memory and to LDS, and the workgroup then
+// forms out[t] = residual[t] + sum_j w[t,j] y[t,j] for its rows with the same
+// fused multiply-add chain as the combine kernel.  No workgroup depends on
+// another.
+#ifndef MOE_ROW_TILE
+#define MOE_ROW_TILE 8
+#endif
+constexpr int kRowTile = MOE_ROW_TILE;  // 8 or 16: one row sum per 2 or 1 of a position's 16 lanes
+static_assert(kRowTile == 8 || kRowTile == 16, "rows per down workgroup");
+#ifndef MOE_ROW_WAVES
+#define MOE_ROW_WAVES 8
+#endif
+constexpr int kRowWaves = MOE_ROW_WAVES;
+constexpr int kRowThreads = 64 * kRowWaves;
 constexpr int kDecodeMaxRows = kDescT * kMaxK;  // routed rows a folded combine can hold (192)
 
-// pp: sorted positions below T*k, loaded unconditionally (so that no load
-// waits for the routed-row count); ok: whether the position is a routed row,
-// the only rows whose results are stored.  The expert id read for a position
+// The positions pbase .. pbase + 3 (lane group qq = lane / 16 takes pbase +
+// qq) over the tile's rows n0 .. n0 + kRowTile - 1.  Positions below T*k are read
+// unconditionally (so that no load waits for the routed-row count; the last
+// one stands in for positions past T*k); nr, the routed-row count, is
+// compared only where results are stored.  The expert id read for a position
 // past the routed rows is stale workspace, clamped into [0, E) so every load
-// stays inside the layer.
-template <int BITS, int NIT, bool YBF16>
-__device__ __forceinline__ void down_rows_items(const DecodeArgs& A, const int (&pp)[NIT], const bool (&ok)[NIT],
-                                                int n0, float* ylds) {
-  const int lane = threadIdx.x & 63, sl = lane >> 4, gl = lane & 15;
+// stays inside the layer.  Each row's sum goes through the same operations as
+// in any other split of the rows over lanes (the same 16 chunk partials, the
+// same pairing of lanes at each reduction level).
+template <int BITS, bool YBF16>
+__device__ __forceinline__ void down_rows_pass(const DecodeArgs& A, int pbase, int nmax, int nr, int n0,
+                                               float* ylds) {
+  const int lane = threadIdx.x & 63, qq = lane >> 4, gl = lane & 15;
   const int64_t rcb = (int64_t)A.I * BITS / 8, rsb = (int64_t)(A.I / 32) * 4;
-  int aa[NIT];
-  bool res[NIT];
-  int64_t pr[NIT];
-  const uint8_t* blob[NIT];
+  const int pq = pbase + qq;
+  const int64_t pr = min(pq, nmax - 1);
+  const int2 ra = *reinterpret_cast<const int2*>(A.rows + 2 * pr);  // (expert, assignment)
+  const int e = min(max(ra.x, 0), A.E - 1);
+  const int aa = ra.y;
+  const int idx = A.pos_slot ? A.pos_slot[pr] : resident_index(A, e);
+  const bool res = idx >= 0;
+  const uint8_t* blob = A.base + (int64_t)(res ? idx : 0) * A.stride;
+  int64_t nrow[kRowTile];
 #pragma unroll
-  for (int q = 0; q < NIT; ++q) {
-    pr[q] = pp[q];
-    const int e = min(max(A.rows[2 * pr[q]], 0), A.E - 1);
-    aa[q] = A.rows[2 * pr[q] + 1];
-    const int idx = A.pos_slot ? A.pos_slot[pr[q]] : resident_index(A, e);
-    res[q] = idx >= 0;
-    blob[q] = A.base + (int64_t)(res[q] ? idx : 0) * A.stride;
-  }
-  float part[NIT][2];
+  for (int r = 0; r < kRowTile; ++r) nrow[r] = min(n0 + r, A.H - 1);
+  float part[kRowTile];
 #pragma unroll
-  for (int q = 0; q < NIT; ++q) part[q][0] = part[q][1] = 0.f;
+  for (int r = 0; r < kRowTile; ++r) part[r] = 0.f;
   const int cpl = A.I / 512;
   for (int cc = 0; cc < cpl; ++cc) {
     const int chunk = gl + 16 * cc;
-    XChunk<true> hc[NIT];
-#pragma unroll
-    for (int q = 0; q < NIT; ++q) {
-      const size_t o = (size_t)pr[q] * A.I + 32 * chunk;
+    XChunk<true> hc;
+    {
+      const size_t o = (size_t)pr * A.I + 32 * chunk;
       const uint4* qh = reinterpret_cast<const uint4*>(A.hh + o);
       const uint4* ql = reinterpret_cast<const uint4*>(A.hl + o);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint4 u = qh[i], v = ql[i];
-        hc[q].hi[4 * i + 0] = u.x;
-        hc[q].hi[4 * i + 1] = u.y;
-        hc[q].hi[4 * i + 2] = u.z;
-        hc[q].hi[4 * i + 3] = u.w;
-        hc[q].lo[4 * i + 0] = v.x;
-        hc[q].lo[4 * i + 1] = v.y;
-        hc[q].lo[4 * i + 2] = v.z;
-        hc[q].lo[4 * i + 3] = v.w;
+        hc.hi[4 * i + 0] = u.x;
+        hc.hi[4 * i + 1] = u.y;
+        hc.hi[4 * i + 2] = u.z;
+        hc.hi[4 * i + 3] = u.w;
+        hc.lo[4 * i + 0] = v.x;
+        hc.lo[4 * i + 1] = v.y;
+        hc.lo[4 * i + 2] = v.z;
+        hc.lo[4 * i + 3] = v.w;
       }
     }
-    uint32_t code[NIT][2][BITS], smw[NIT][2];
+    uint32_t code[kRowTile][BITS], smw[kRowTile];
 #pragma unroll
-    for (int q = 0; q < NIT; ++q)
+    for (int r = 0; r < kRowTile; ++r) {
+      load_codes<BITS>(code[r], blob + A.off_dc + nrow[r] * rcb + chunk * (4 * BITS));
+      smw[r] = *reinterpret_cast<const uint32_t*>(blob + A.off_ds + nrow[r] * rsb + chunk * 4);
+    }
+    float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int64_t n = min(n0 + 4 * r + sl, A.H - 1);
-        load_codes<BITS>(code[q][r], blob[q] + A.off_dc + n * rcb + chunk * (4 * BITS));
-        smw[q][r] = *reinterpret_cast<const uint32_t*>(blob[q] + A.off_ds + n * rsb + chunk * 4);
-      }
+    for (int i = 0; i < 16; ++i) {
+      sum = dot2(hc.hi[i], 0x3F803F80u, sum);
+      sum = dot2(hc.lo[i], 0x3F803F80u, sum);
+    }
+    hc.sum = sum;
 #pragma unroll
-    for (int q = 0; q < NIT; ++q) {
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sum = dot2(hc[q].hi[i], 0x3F803F80u, sum);
-        sum = dot2(hc[q].lo[i], 0x3F803F80u, sum);
-      }
-      hc[q].sum = sum;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float sc = f16lo(smw[q][r]), mn = f16hi(smw[q][r]);
-        const float mo = mn - 128.0f * sc;
-        part[q][r] = __builtin_fmaf(sc, chunk_dot<BITS, true>(code[q][r], hc[q]), __builtin_fmaf(mo, sum, part[q][r]));
-      }
+    for (int r = 0; r < kRowTile; ++r) {
+      const float sc = f16lo(smw[r]), mn = f16hi(smw[r]);
+      const float mo = mn - 128.0f * sc;
+      part[r] = __builtin_fmaf(sc, chunk_dot<BITS, true>(code[r], hc), __builtin_fmaf(mo, sum, part[r]));
     }
   }
-#pragma unroll
-  for (int q = 0; q < NIT; ++q) {
-    float v[2] = {part[q][0], part[q][1]};
-    reduce_scatter<2, 1, 3, 0>(v, lane);  // lanes with bit 3 clear hold row step 0, set: row step 1
-    if ((gl & 7) == 0 && ok[q]) {
-      const int r = gl >> 3, n = n0 + 4 * r + sl;
-      if (n < A.H) {
-        const float val = res[q] ? v[0] : __builtin_nanf("");
-        float yv = val;
-        if constexpr (YBF16) {
-          const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)val);
-          reinterpret_cast<uint16_t*>(A.y)[(int64_t)aa[q] * A.H + n] = b;
-          yv = __uint_as_float((uint32_t)b << 16);
-        } else {
-          reinterpret_cast<float*>(A.y)[(int64_t)aa[q] * A.H + n] = val;
-        }
-        if (ylds) ylds[aa[q] * kRowTile + 4 * r + sl] = yv;
+  // lanes of a position's 16 end with the sum of row gl * kRowTile / 16
+  reduce_scatter<kRowTile, 1, 3, 0>(part, lane);
+  constexpr int kLanesPerRow = 16 / kRowTile;
+  if (gl % kLanesPerRow == 0 && pq < nr) {
+    const int r = gl / kLanesPerRow, n = n0 + r;
+    if (n < A.H) {
+      const float val = res ? part[0] : __builtin_nanf("");
+      float yv = val;
+      if constexpr (YBF16) {
+        const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)val);
+        reinterpret_cast<uint16_t*>(A.y)[(int64_t)aa * A.H + n] = b;
+        yv = __uint_as_float((uint32_t)b << 16);
+      } else {
+        reinterpret_cast<float*>(A.y)[(int64_t)aa * A.H + n] = val;
       }
+      if (ylds) ylds[aa * kRowTile + r] = yv;
     }
   }
 }
@@ -947,39 +973,35 @@ template <int BITS, bool YBF16>
 __device__ __forceinline__ void ffn_down_rows_body(const DecodeArgs& A) {
   __shared__ float ylds[kDecodeMaxRows * kRowTile];
   __shared__ float wl[kDecodeMaxRows];
+  warm_kernargs<sizeof(DecodeArgs)>();
   const int wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * kRowTile;
   const bool fold = A.out != nullptr;
-  // the combine's inputs, loaded before the routed rows
+  // The combine's inputs are loaded first but used only after the routed
+  // rows, so no wait for them stands before the rows' loads.
   const int ct = threadIdx.x / kRowTile, cr = threadIdx.x % kRowTile;
   const bool comb = fold && ct < A.T && n0 + cr < A.H;
-  if (fold && (int)threadIdx.x < A.T * A.k) wl[threadIdx.x] = A.w[threadIdx.x];
-  float acc = 0.f;
-  if (comb) {
-    if (A.residual)
-      acc = A.r_bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(A.residual)[(size_t)ct * A.H + n0 + cr]
-                                       << 16)
-                     : reinterpret_cast<const float*>(A.residual)[(size_t)ct * A.H + n0 + cr];
+  const bool wmine = fold && (int)threadIdx.x < A.T * A.k;
+  float wv = 0.f;
+  if (wmine) wv = A.w[threadIdx.x];
+  uint32_t rraw = 0;  // residual: fp32 bits, or bf16 bits in the low half
+  if (comb && A.residual) {
+    const size_t o = (size_t)ct * A.H + n0 + cr;
+    if (A.r_bf16) rraw = reinterpret_cast<const uint16_t*>(A.residual)[o];
+    else rraw = reinterpret_cast<const uint32_t*>(A.residual)[o];
   }
   // Routed rows: nr <= T*k (fewer only when dispatch dropped ids).  The loop
-  // runs over T*k positions so that the row loads do not wait for nr.
-  const int nr = *A.nrows, nmax = A.T * A.k;
+  // runs over T*k positions so that the row loads do not wait for nr, which
+  // is read with a vector load (a scalar load's wait would come before them).
+  const int nr = __builtin_nontemporal_load(A.nrows), nmax = A.T * A.k;
   float* yl = fold ? ylds : nullptr;
-  for (int p = wave; p < nmax; p += 2 * kRowWaves) {
-    const int p2 = p + kRowWaves;
-    if (p2 < nmax) {
-      const int pp[2] = {p, p2};
-      const bool ok[2] = {p < nr, p2 < nr};
-      down_rows_items<BITS, 2, YBF16>(A, pp, ok, n0, yl);
-    } else {
-      const int pp[1] = {p};
-      const bool ok[1] = {p < nr};
-      down_rows_items<BITS, 1, YBF16>(A, pp, ok, n0, yl);
-    }
-  }
+  for (int pbase = 4 * wave; pbase < nmax; pbase += 4 * kRowWaves) down_rows_pass<BITS, YBF16>(A, pbase, nmax, nr, n0, yl);
   if (!fold) return;
+  if (wmine) wl[threadIdx.x] = wv;
   __syncthreads();
   if (comb) {
+    float acc = 0.f;
+    if (A.residual) acc = A.r_bf16 ? __uint_as_float(rraw << 16) : __uint_as_float(rraw);
     for (int j = 0; j < A.k; ++j) acc = __builtin_fmaf(wl[ct * A.k + j], ylds[(ct * A.k + j) * kRowTile + cr], acc);
     const size_t o = (size_t)ct * A.H + n0 + cr;
     A.out[o] = acc;
@@ -992,7 +1014,7 @@ __device__ __forceinline__ void ffn_down_rows_body(const DecodeArgs& A) {
 }
 
 template <int BITS, bool YBF16>
-__global__ __launch_bounds__(1024) void ffn_down_rows_kernel(DecodeArgs A) {
+__global__ __launch_bounds__(kRowThreads) void ffn_down_rows_kernel(DecodeArgs A) {
   ffn_down_rows_body<BITS, YBF16>(A);
 }
 
@@ -1084,7 +1106,7 @@ moe_status launch_wide(DecodeArgs& a, int max_active, hipStream_t s) {
            dim3((unsigned)(max_active * a.TA)), dim3(256), 0, s, a);
   if (moe_status st = check_launch("ffn_gateup")) return st;
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
-           dim3(64 * kRowWaves), 0, s, a);
+           dim3(kRowThreads), 0, s, a);
   return check_launch("ffn_down");
 }
 
@@ -1098,7 +1120,7 @@ moe_status launch_wide_stage(DecodeArgs& a, const StageArgs& g, int max_active, 
            dim3((unsigned)(g.ncw + max_active * a.TA)), dim3(256), 0, s, a, g);
   if (moe_status st = check_launch("ffn_gateup_stage")) return st;
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
-           dim3(64 * kRowWaves), 0, s, a);
+           dim3(kRowThreads), 0, s, a);
   return check_launch("ffn_down");
 }
 
@@ -1143,6 +1165,7 @@ constexpr int kRoutedNI = BITS >= 3 ? (SPLIT ? 2 : MOE_ROUTED_NI4) : (SPLIT ? MO
 template <int BITS, bool SPLIT, int EPL, int NI>
 __global__ __launch_bounds__(256) void ffn_route_gateup_kernel(DecodeArgs A, RouteOut R) {
   __shared__ dev::RouterLds L;
+  warm_kernargs<sizeof(DecodeArgs) + sizeof(RouteOut)>();
   if (blockIdx.x == 0) {
     dev::decode_route_lds<EPL, 256>(R.logits, A.T, A.E, A.k, L);
     dev::decode_route_write<256>(L, A.T, A.E, A.k, R.ids, R.w, R.offsets, R.sorted_assign, R.assign_pos, R.active,
@@ -1163,7 +1186,7 @@ moe_status launch_wide_routed(DecodeArgs& a, const RouteOut& r, int max_active, 
            dim3((unsigned)(1 + max_active * a.TA)), dim3(256), 0, s, a, r);
   if (moe_status st = check_launch("ffn_route_gateup")) return st;
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
-           dim3(64 * kRowWaves), 0, s, a);
+           dim3(kRowThreads), 0, s, a);
   return check_launch("ffn_down");
 }
 
@@ -1273,7 +1296,7 @@ __global__ __launch_bounds__(256) void ffn_route_resolve_gateup_kernel(DecodeArg
 // the resolve's outcome into the table state (nothing reads the old state any
 // more).
 template <int BITS, bool YBF16>
-__global__ __launch_bounds__(1024) void ffn_down_rows_commit_kernel(DecodeArgs A, SlotDevArgs SA,
+__global__ __launch_bounds__(kRowThreads) void ffn_down_rows_commit_kernel(DecodeArgs A, SlotDevArgs SA,
                                                                     const int32_t* record) {
   if (blockIdx.x == 0 && threadIdx.x == 0) dev::slot_record_commit(SA, record);
   ffn_down_rows_body<BITS, YBF16>(A);
@@ -1288,7 +1311,7 @@ moe_status launch_resolve_routed(DecodeArgs& a, const RouteOut& r, const StageAr
   if (moe_status st = check_launch("ffn_route_resolve_gateup")) return st;
   a.pos_slot = pos_slot;
   launch_k(MOE_KERNEL_GEMV_DOWN, ffn_down_rows_commit_kernel<BITS, YBF16>, dim3((unsigned)ceil_div(a.H, kRowTile)),
-           dim3(64 * kRowWaves), 0, s, a, sa, (const int32_t*)record);
+           dim3(kRowThreads), 0, s, a, sa, (const int32_t*)record);
   return check_launch("ffn_down");
 }
 
@@ -1402,7 +1425,7 @@ moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x
                                  moe_dtype y_t, const FoldedCombine& fc, hipStream_t s, const MissStage* ms) {
   DecodeArgs a = make_args(q, x, T, k, sorted_assign, n_active, W, y);
   if (fc.out) {
-    if (!wide_shape(q.H, q.I) || (int64_t)T * k > kDecodeMaxRows || T * kRowTile > 64 * kRowWaves)
+    if (!wide_shape(q.H, q.I) || (int64_t)T * k > kDecodeMaxRows || T * kRowTile > kRowThreads)
       return fail(MOE_EUNSUPPORTED, "combine cannot be folded for this shape");
     a.w = fc.w;
     a.residual = fc.residual;
@@ -1440,7 +1463,7 @@ moe_status launch_ffn_gemv_steps(const moe_qlayer& q, const void* x, moe_dtype x
 }
 
 bool decode_routes_in_gateup(int H, int I, int T, int k) {
-  return wide_shape(H, I) && (int64_t)T * k <= dev::kDecodeMaxN && T * kRowTile <= 64 * kRowWaves;
+  return wide_shape(H, I) && (int64_t)T * k <= dev::kDecodeMaxN && T * kRowTile <= kRowThreads;
 }
 
 moe_status launch_decode_routed(const moe_qlayer& q, const float* logits, const void* x, moe_dtype x_t, int T, int k,
