@@ -56,7 +56,7 @@ FETCH_SCALE = 262144.0 / 131093.4
 WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp", "slot_dev.hpp"],
-                    "sha": "e4fc07354f2fefb9", "fetch_kib": 7625.125, "write_kib": 62.9375},
+                    "sha": "1656006d9d5ef094", "fetch_kib": 7632.875, "write_kib": 62.9375},
     "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "c4ba23cd1b4d1045", "fetch_kib": 295328.3125,
                     "write_kib": 81931.78125},
 }
