@@ -888,6 +888,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   }
   const uint8_t* blob = A.base + (int64_t)idx * A.stride;
 
+  // The epilogue's row information, fetched under the K-loop: thread t < rows
+  // holds tile row t's assignment (issued here) and its token's exponent
+  // (issued after the loop's first barrier, when the assignment has arrived),
+  // handed to the lanes of that row through LDS after the loop.
+  const bool ri_on = tid < BM && tid < rows;
+  int ri_a = 0, ri_e = 0;
+  if (ri_on) ri_a = A.sorted_assign[p_begin + tid];
+
   // ---- activation tile: two 16-byte chunks per thread per K-step ----------------
   int a_voff[A_CHUNKS], a_lds[A_CHUNKS];
 #pragma unroll
@@ -1076,6 +1084,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     store_a(sa0, 0);
     store_bchunk(st, 0);
     __syncthreads();
+    if (ri_on) ri_e = A.xexp[ri_a / A.k];
     load_a(sa0, min(2, KS - 1));
     load_bchunk(st, min(CK, KS - CK));
     f16x8_t ao0[4], ao1[4], bo[2], bo2[2];
@@ -1091,11 +1100,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     auto step = [&](int buf, int nbb, int nksl, const uint4 (&a_next)[A_CHUNKS], auto&& pre) {
       mfma_half(nvc, bo, ao0, [&] {
         read_a(buf, 1, ao1);
+        read_bstep(ns, nbb, nksl);
         dec_half(cs, 1, d, bo2);
       });
       __builtin_amdgcn_sched_barrier(0);
       mfma_half(nvc, bo2, ao1, [&] {
-        read_bstep(ns, nbb, nksl);
         tables(ns, d);
         dec_half(ns, 0, d, bo);
       });
@@ -1136,16 +1145,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   }
 
   // ---- epilogue: lane holds token row 32 fm + lane % 32 of the tile ----------------
+  __syncthreads();  // every wave is past its last activation reads
+  int2* lds_ri = reinterpret_cast<int2*>(&lds_a[0][0]);
+  if (ri_on) lds_ri[tid] = make_int2(ri_a, ri_e);
+  __syncthreads();
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm) {
     const int m = 32 * fm + jl;
     if (fm >= nv || m >= rows) continue;
+    const int2 ri = lds_ri[m];  // (assignment, token exponent) of row m
     if constexpr (GATEUP) {
       // accumulator 4 g + s: gate of i = base + 2 g + s; 4 g + 2 + s: its up (s = 0, 1); all
       // 2^-e_t times their true values: h' = g' * sigmoid(g' * 2^e_t) * u' = h * 2^(-2 e_t)
       _Float16* hrow = reinterpret_cast<_Float16*>(A.out) + (size_t)(p_begin + m) * A.I;
-      const int ex = A.xexp[A.sorted_assign[p_begin + m] / A.k];
-      const float cz = __builtin_amdgcn_ldexpf(-1.4426950408889634f, ex);  // -log2(e) 2^e_t, exact
+      const float cz = __builtin_amdgcn_ldexpf(-1.4426950408889634f, ri.y);  // -log2(e) 2^e_t, exact
       float h[2][8], mx = 0.f;
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn)
@@ -1175,8 +1188,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                        pack_f16(h[fn][6], h[fn][7]));
       }
     } else {
-      const int64_t a = A.sorted_assign[p_begin + m];
-      const int ey = 2 * A.xexp[a / A.k];
+      const int64_t a = ri.x;
+      const int ey = 2 * ri.y;
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn) {
         const int n0 = nt * BN + 64 * wave + 32 * fn + 16 * hh;
