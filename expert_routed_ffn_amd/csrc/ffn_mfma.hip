@@ -61,9 +61,11 @@
 // (2c, 2c+1 per halfword), i.e. ~2 VALU ops per weight; 4- and 3-bit codes
 // decode in packed fp16 (see below), about 2.5 VALU ops per weight.
 //
-// A small prep kernel turns (n_active, active, offsets) into the list of
-// (expert slot, first row) M-tiles; the GEMM grid is sized for the worst case
-// and blocks past the list's end exit at once.
+// A small prep kernel turns (n_active, active, offsets, slot map) into the
+// list of M-tiles, each its expert's blob index, first sorted row and row
+// count in one 16-byte entry, so a workgroup starts from one load instead of a
+// chain of four; the GEMM grid is sized for the worst case and blocks past the
+// list's end exit at once.
 #include <type_traits>
 
 #include "internal.hpp"
@@ -193,14 +195,15 @@ __device__ __forceinline__ void decode16_b3(uint32_t lo, uint32_t hi, uint32_t s
   }
 }
 
-struct TileInfo {
-  int32_t slot, m0;
+struct TileInfo {  // one M-tile: its expert's blob index and its sorted rows p_begin .. p_begin + rows
+  int32_t idx, p_begin, rows, pad;
 };
 
 // Build the M-tile list: for each active slot, ceil(n_e / BM) tiles.
 __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ active,
-                                                          const int32_t* __restrict__ n_active, int BM,
+                                                          const int32_t* __restrict__ n_active,
+                                                          const int32_t* __restrict__ slot_map, int BM,
                                                           TileInfo* __restrict__ tiles, int32_t* __restrict__ count) {
   __shared__ int sh[1024 / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -208,11 +211,13 @@ __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t* __restr
   int running = 0;
   for (int base = 0; base < na; base += 1024) {
     const int s = base + tid;
-    int mt = 0, ne = 0;
+    int mt = 0, ne = 0, p0 = 0, idx = 0;
     if (s < na) {
       const int e = active[s];
-      ne = offsets[e + 1] - offsets[e];
+      p0 = offsets[e];
+      ne = offsets[e + 1] - p0;
       mt = (ne + BM - 1) / BM;
+      idx = slot_map ? slot_map[e] : e;
     }
     int inc = mt;
 #pragma unroll
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t* __restr
       total += sh[w];
     }
     const int start = running + before + inc - mt;
-    for (int j = 0; j < mt; ++j) tiles[start + j] = TileInfo{s, j * BM};
+    for (int j = 0; j < mt; ++j) tiles[start + j] = TileInfo{idx, p0 + j * BM, min(BM, ne - j * BM), 0};
     running += total;
     __syncthreads();
   }
@@ -299,14 +304,11 @@ __global__ __launch_bounds__(256) void to_f16_kernel(const void* __restrict__ x,
 struct GemmArgs {
   const uint8_t* base;
   int64_t stride;
-  const int32_t* slot_map;
   int H, I, k;
   int64_t off_c0, off_s0, off_c1, off_s1;  // gate/up: Wg and Wu planes; down: Wd planes in c0/s0
   const _Float16* a_src;                   // x [T x H] (gate/up) or h [n x I] (down), fp16
   int64_t a_zero_row;                      // T or n: an all-zero row of a_src
-  const int32_t* offsets;
   const int32_t* sorted_assign;
-  const int32_t* active;
   const TileInfo* tiles;
   const int32_t* tile_count;
   int n_tiles_n;
@@ -359,11 +361,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MOE_MFMA_WAV
     nt = j % A.n_tiles_n;
     if (tile_idx >= *A.tile_count) return;
   }
-  const TileInfo ti = A.tiles[tile_idx];
-  const int e = A.active[ti.slot];
-  const int p_begin = A.offsets[e] + ti.m0;
-  const int rows = min(BM, A.offsets[e + 1] - p_begin);
-  const int idx = A.slot_map ? A.slot_map[e] : e;
+  const TileInfo ti = A.tiles[tile_idx];  // one 16-byte load: no chain through active, offsets and the map
+  const int p_begin = ti.p_begin, rows = ti.rows, idx = ti.idx;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = __builtin_amdgcn_readfirstlane(wave >> 1), wn = wave & 1;
   // Wave row wm owns the 16-row groups wm, wm + WMR, wm + 2 WMR, ... of the
@@ -858,11 +857,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     nt = jb % A.n_tiles_n;
     if (tile_idx >= *A.tile_count) return;
   }
-  const TileInfo ti = A.tiles[tile_idx];
-  const int e = A.active[ti.slot];
-  const int p_begin = A.offsets[e] + ti.m0;
-  const int rows = min(BM, A.offsets[e + 1] - p_begin);
-  const int idx = A.slot_map ? A.slot_map[e] : e;
+  const TileInfo ti = A.tiles[tile_idx];  // one 16-byte load: no chain through active, offsets and the map
+  const int p_begin = ti.p_begin, rows = ti.rows, idx = ti.idx;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, jl = lane & 31;
@@ -1286,19 +1282,16 @@ moe_status launch_all(const moe_qlayer& q, const BlobLayout& L, const void* x, b
     to_f16_kernel<false><<<cblocks, 256, 0, s>>>(x, T, q.H / 8, reinterpret_cast<uint4*>(W.x16), W.xexp, z1, q.H / 8,
                                                  z2, q.I / 8, W.clip);
   if (moe_status st = check_launch("mfma_to_f16")) return st;
-  mfma_tiles_kernel<<<1, 1024, 0, s>>>(offsets, active, n_active, kBM, W.tiles, W.count);
+  mfma_tiles_kernel<<<1, 1024, 0, s>>>(offsets, active, n_active, q.slot_map, kBM, W.tiles, W.count);
   if (moe_status st = check_launch("mfma_tiles")) return st;
 
   GemmArgs a;
   a.base = reinterpret_cast<const uint8_t*>(q.base);
   a.stride = q.stride;
-  a.slot_map = q.slot_map;
   a.H = q.H;
   a.I = q.I;
   a.k = k;
-  a.offsets = offsets;
   a.sorted_assign = sorted_assign;
-  a.active = active;
   a.tiles = W.tiles;
   a.tile_count = W.count;
   a.xexp = W.xexp;
