@@ -57,8 +57,8 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp", "slot_dev.hpp"],
                     "sha": "1656006d9d5ef094", "fetch_kib": 7632.875, "write_kib": 62.9375},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "c4ba23cd1b4d1045", "fetch_kib": 295328.3125,
-                    "write_kib": 81931.78125},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "2dba9dbef942dbde", "fetch_kib": 297891.5625,
+                    "write_kib": 81923.4375},
 }
 
 
