@@ -56,7 +56,7 @@ FETCH_SCALE = 262144.0 / 131093.4
 WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp", "slot_dev.hpp"],
-                    "sha": "1d44f514382a9a39", "fetch_kib": 7632.875, "write_kib": 62.9375},
+                    "sha": "f9f3b89b37ce3455", "fetch_kib": 7632.875, "write_kib": 62.9375},
     "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "2dba9dbef942dbde", "fetch_kib": 297891.5625,
                     "write_kib": 81923.4375},
 }

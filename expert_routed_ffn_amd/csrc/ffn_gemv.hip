@@ -165,12 +165,13 @@ __device__ __forceinline__ float chunk_dot(const uint32_t (&code)[BITS], const X
 }
 
 // Weight codes, and the gate and up scale/min words, are loaded as streaming
-// (nontemporal) accesses: a decode step reads each of them once (the down
-// codes of an expert's several positions within one workgroup's burst), and
-// they then do not displace the activations, h and routing data that the
+// (nontemporal) accesses: a decode step reads each of them once (a down
+// workgroup reads the codes of an expert's several positions back to back),
+// and they then do not displace the activations, h and routing data that the
 // workgroups re-read from the L2.  Decode/verify layer step 19.46 -> 18.34 us
-// on one box; streaming loads of the down scale/min words as well measured
-// slower (18.9 us).
+// on one box.  The down scale/min words (two rows per cache line, read by
+// different lane groups) measured slower that way (18.9 us) and keep ordinary
+// loads.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 template <bool NT = false>
