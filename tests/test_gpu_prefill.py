@@ -147,6 +147,44 @@ def test_mfma_small_cases_full(moe, E, k, H, I, T, bits, x_dtype, zipf):
     assert ey <= PREFILL_TOL and eo <= PREFILL_TOL
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_mfma_through_slot_map(moe, bits):
+    """The MFMA path with the experts placed in a slot pool by a map (the M-tile
+    list resolves each expert's slot): experts in permuted slots give the same
+    bits as the plain layout, and an expert marked not resident gives NaN y rows
+    for its assignments and leaves every other row unchanged."""
+    import torch
+    w = _custom(8, 2, 256, 128, 300, bits, "bf16", 0.5)
+    x, lg, ex = w.x(), w.logits(), w.experts()
+    ref = _run(moe, w, x, lg, ex)
+    ids_ref, y_ref = ref[0], to_host(ref[3])
+    hit = np.unique(to_host(ids_ref))
+    gone = int(hit[len(hit) // 2])  # a routed expert that is then taken out
+    eb = w.expert_bytes
+    pool = np.zeros((w.E + 1) * eb, np.uint8)  # slot 0 stays unused
+    smap = np.empty(w.E, np.int32)
+    for e in range(w.E):
+        slot = w.E - e  # reversed placement
+        smap[e] = slot
+        pool[slot * eb:(slot + 1) * eb] = ex.reshape(w.E, eb)[e]
+    for case in ("all", "gone"):
+        m = smap.copy()
+        if case == "gone":
+            m[gone] = -1
+        layer = moe.ExpertLayer(w.E, w.H, w.I, w.bits, to_dev(pool), slot_map=torch.from_numpy(m).cuda())
+        ids, wt, d, y, out = moe.layer_forward(layer, to_dev_x(x), to_dev(lg), w.k, path="mfma")
+        torch.cuda.synchronize()
+        yy = to_host(y)
+        assert np.array_equal(to_host(ids), to_host(ids_ref))
+        sel = to_host(ids) == gone  # [T, k] assignments to the expert taken out
+        if case == "all":
+            assert np.array_equal(yy, y_ref)
+        else:
+            assert sel.any() and np.all(np.isnan(yy[sel]))
+            assert np.array_equal(yy[~sel], y_ref[~sel])
+        print(f"{w.name} {case}: {int(sel.sum())} assignments to expert {gone}")
+
+
 def test_decode_and_prefill_paths_agree(moe):
     w = synth.decode_verify()
     lg = w.logits()
