@@ -57,11 +57,11 @@ WRITE_SCALE = 1.0
 TRAFFIC = {
     "gemv_gateup": {"sources": ["ffn_gemv.hip", "route_dispatch_dev.hpp", "slot_dev.hpp"],
                     "sha": "f9f3b89b37ce3455", "fetch_kib": 7632.875, "write_kib": 62.9375},
-    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "2dba9dbef942dbde", "fetch_kib": 297891.5625,
-                    "write_kib": 81923.4375},
+    "mfma_gateup": {"sources": ["ffn_mfma.hip"], "sha": "331d90259eb66f12", "fetch_kib": 292906.25,
+                    "write_kib": 81920.625},
     # the same kernel on the chunk whose router bias is scaled by 0.21 (every expert hit)
-    "mfma_gateup_flat": {"sources": ["ffn_mfma.hip"], "sha": "2dba9dbef942dbde", "fetch_kib": 547214.625,
-                         "write_kib": 81942.5},
+    "mfma_gateup_flat": {"sources": ["ffn_mfma.hip"], "sha": "331d90259eb66f12", "fetch_kib": 520170.75,
+                         "write_kib": 81927.15625},
 }
 
 
