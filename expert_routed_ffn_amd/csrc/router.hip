@@ -95,28 +95,35 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
 
 // ---- MFMA GEMM --------------------------------------------------------------
 
-constexpr int kTile = 128;  // tokens and experts per workgroup tile
-constexpr int kBK = 32;     // K-step: one MFMA's K
+#ifndef MOE_ROUTER_TM
+#define MOE_ROUTER_TM 64
+#endif
+constexpr int kTileM = MOE_ROUTER_TM;  // tokens per workgroup tile (64: 512 workgroups for 8,192 tokens)
+constexpr int kTile = 128;             // experts per workgroup tile
+constexpr int kFM = kTileM / 32;       // 16-token fragments per wave
+constexpr int kBK = 32;                // K-step: one MFMA's K
+static_assert(kTileM == 64 || kTileM == 128, "tokens per router tile");
 
 // 64-byte LDS rows of 32 bf16; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 3)
 // (conflict-free for the fragment reads below).
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 32 + ((chunk ^ ((row >> 1) & 3)) * 8); }
 
-// Grid: (ceil(T / 128), ceil(E / 128)); 256 threads = 4 waves in a 2 x 2 grid,
-// each owning 64 tokens x 64 experts (4 x 4 fragments).  Rows past T or E read
-// the last valid row and are never stored.
+// Grid: (ceil(T / kTileM), ceil(E / 128)); 256 threads = 4 waves in a 2 x 2
+// grid, each owning kTileM / 2 tokens x 64 experts (kFM x 4 fragments).  Rows
+// past T or E read the last valid row and are never stored.  With 64-token
+// tiles the 8,192-token chunk runs 512 workgroups, two per CU.
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr, int T, int H, int E,
                                                           float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_x[2][kTile * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_x[2][kTileM * 32];
   __shared__ __attribute__((aligned(16))) uint16_t lds_w[2][kTile * 32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * kTile, n0 = blockIdx.y * kTile;
+  const int m0 = blockIdx.x * kTileM, n0 = blockIdx.y * kTile;
   const int KS = H / kBK;
 
   // loads: thread chunks c = tid and tid + 256: rows r0 = tid / 4 and r0 + 64,
-  // 16-byte chunk tid % 4 of each
+  // 16-byte chunk tid % 4 of each (x takes the second row only for 128-token tiles)
   const int r0 = tid >> 2, r1 = r0 + 64, ch = tid & 3;
   const uint16_t* x0 = x + (size_t)min(m0 + r0, T - 1) * H + ch * 8;
   const uint16_t* x1 = x + (size_t)min(m0 + r1, T - 1) * H + ch * 8;
@@ -128,31 +135,36 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   };
   auto load = [&](int ks) {
     const size_t k = (size_t)ks * kBK;
-    return Stage{*reinterpret_cast<const uint4*>(x0 + k), *reinterpret_cast<const uint4*>(x1 + k),
-                 *reinterpret_cast<const uint4*>(w0 + k), *reinterpret_cast<const uint4*>(w1 + k)};
+    Stage st;
+    st.x0 = *reinterpret_cast<const uint4*>(x0 + k);
+    st.x1 = kTileM == 128 ? *reinterpret_cast<const uint4*>(x1 + k) : make_uint4(0, 0, 0, 0);
+    st.w0 = *reinterpret_cast<const uint4*>(w0 + k);
+    st.w1 = *reinterpret_cast<const uint4*>(w1 + k);
+    return st;
   };
   auto store = [&](const Stage st, int buf) {
     *reinterpret_cast<uint4*>(&lds_x[buf][o0]) = st.x0;
-    *reinterpret_cast<uint4*>(&lds_x[buf][o1]) = st.x1;
+    if (kTileM == 128) *reinterpret_cast<uint4*>(&lds_x[buf][o1]) = st.x1;
     *reinterpret_cast<uint4*>(&lds_w[buf][o0]) = st.w0;
     *reinterpret_cast<uint4*>(&lds_w[buf][o1]) = st.w1;
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[kFM][4];
 #pragma unroll
-  for (int fi = 0; fi < 4; ++fi)
+  for (int fi = 0; fi < kFM; ++fi)
 #pragma unroll
     for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fq = lane >> 4;
   auto mma = [&](int buf) {
-    bf16x8_t xf[4], wf[4];
+    bf16x8_t xf[kFM], wf[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      xf[f] = *reinterpret_cast<const bf16x8_t*>(&lds_x[buf][lds_off(64 * wm + 16 * f + fr, fq)]);
+    for (int f = 0; f < kFM; ++f)
+      xf[f] = *reinterpret_cast<const bf16x8_t*>(&lds_x[buf][lds_off((kTileM / 2) * wm + 16 * f + fr, fq)]);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
       wf[f] = *reinterpret_cast<const bf16x8_t*>(&lds_w[buf][lds_off(64 * wn + 16 * f + fr, fq)]);
-    }
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi)
+    for (int fi = 0; fi < kFM; ++fi)
 #pragma unroll
       for (int fj = 0; fj < 4; ++fj)
         acc[fi][fj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[fj], xf[fi], acc[fi][fj], 0, 0, 0);
@@ -179,8 +191,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   // lane: token 16 fi + (lane & 15), experts 16 fj + 4 (lane >> 4) + r
   const bool vec = (E & 3) == 0;
 #pragma unroll
-  for (int fi = 0; fi < 4; ++fi) {
-    const int t = m0 + 64 * wm + 16 * fi + fr;
+  for (int fi = 0; fi < kFM; ++fi) {
+    const int t = m0 + (kTileM / 2) * wm + 16 * fi + fr;
     if (t >= T) continue;
     float* out = logits + (size_t)t * E;
 #pragma unroll
@@ -207,7 +219,7 @@ moe_status launch_router_logits(const void* x, bool xf32, const uint16_t* wr, in
                                 hipStream_t s) {
   if (!xf32 && T >= kRouterMfmaMinT) {
     launch_k(MOE_KERNEL_ROUTER, router_mfma_kernel,
-             dim3((unsigned)ceil_div(T, kTile), (unsigned)ceil_div(E, kTile)), dim3(256), 0, s,
+             dim3((unsigned)ceil_div(T, kTileM), (unsigned)ceil_div(E, kTile)), dim3(256), 0, s,
              reinterpret_cast<const uint16_t*>(x), wr, T, H, E, logits);
   } else {
     const dim3 grid((unsigned)ceil_div(E, 4), (unsigned)ceil_div(T, kGemvT));
