@@ -39,12 +39,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe.so)")
 
 
+# The host pass of hipcc does not know the device-only feature named in CFLAGS
+# and says so once per file; that line carries no information.
+_HOST_FEATURE_NOTE = "packed-fp32-ops' is not a recognized feature"
+
+
+def _diagnostics(text: str) -> str:
+    return "\n".join(l for l in text.splitlines() if _HOST_FEATURE_NOTE not in l and l.strip())
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
+    diag = _diagnostics(r.stdout + "\n" + r.stderr)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {src}:\n{diag}")
+    if diag:  # real warnings stay visible
+        print(f"hipcc {src}:\n{diag}", file=sys.stderr)
     return obj
 
 

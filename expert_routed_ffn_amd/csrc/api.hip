@@ -173,7 +173,6 @@ static moe_ffn_path resolve_path(moe_ffn_path p, int T, int k) {
 
 size_t moe_expert_ffn_workspace_bytes(const moe_qlayer* q, int T, int k, moe_ffn_path path) {
   if (!q || T < 0 || k < 1) return 0;
-  const int n = T * k;
   if (resolve_path(path, T, k) == MOE_PATH_GEMV) return ffn_gemv_ws_bytes(T, k, q->E, q->H, q->I);
   return ffn_mfma_ws_bytes(T, k, q->E, q->H, q->I);
 }

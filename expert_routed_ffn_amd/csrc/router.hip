@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
                            bf16_lo(wv[u].z), bf16_hi(wv[u].z), bf16_lo(wv[u].w), bf16_hi(wv[u].w)};
 #pragma unroll
       for (int t = 0; t < kGemvT; ++t) {
-        if (t >= nt) break;
+        if (t >= nt) continue;  // (a break would keep the loop from unrolling)
         float xf[8];
         const size_t xi = (size_t)(t0 + t) * H + c;
         if constexpr (XF32) {
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void* __restrict
   }
 #pragma unroll
   for (int t = 0; t < kGemvT; ++t) {
-    if (t >= nt) break;
+    if (t >= nt) continue;
     const float v = wave_sum(acc[t]);
     if (lane == 0) logits[(size_t)(t0 + t) * E + e] = v;
   }
